@@ -1,0 +1,288 @@
+"""Pins of the float64 oracle to facts fixed outside it (CPU only).
+
+Each test names what it pins.  Together they are chosen so that a plausible
+slip in the oracle -- a transposed M or T^-1, a wrong group-to-bit mapping,
+MSB-first bit order, flipped sign polarity, a scale applied per column, a
+dropped block -- fails at least one of them.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import lq_oracle as O
+from bit_lifted_gemv_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _lines(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# ----------------------------------------------------------------- bit-widths
+def test_bitwidth_golden_matches_D_over_d():
+    """Printed bits per weight of every LQ-D/d code equal D/d (to print precision)."""
+    for ln in _lines("bitwidths.txt"):
+        code, D, d, bits = ln.split()
+        D, d = int(D), int(d)
+        assert code == f"LQ-{D}/{d}"
+        assert abs(D / d - float(bits)) <= 0.5 * 10 ** -(len(bits.split(".")[1])) + 1e-12
+
+
+@pytest.mark.parametrize("cfg", synth.CONFIGS, ids=lambda c: c.name)
+def test_bitwidth_from_packed_byte_count(cfg):
+    """8 * bytes(packed W_q) / (m * n) == D / d exactly for every workload shape."""
+    for (m, n) in cfg.shapes:
+        K = synth.lifted_dim(n, cfg.d, cfg.D)
+        ldw = synth.words_per_row(K)
+        assert K % 32 == 0
+        nbytes = m * ldw * 4
+        assert 8 * nbytes * cfg.d == m * n * cfg.D
+
+
+# ----------------------------------------------------------------- sign packing
+def _parse_positions(tok):
+    out = []
+    for part in tok.split():
+        if "-" in part:
+            lo, hi = part.split("-")
+            out.extend(range(int(lo), int(hi) + 1))
+        else:
+            out.append(int(part))
+    return out
+
+
+def test_pack_golden_words():
+    """Hand-worked packed words (LSB-first, bit 1 = +1, zero padding)."""
+    for ln in _lines("pack_known.txt"):
+        K, pos, words = [t.strip() for t in ln.split(";")]
+        K = int(K)
+        signs = -np.ones((1, K), dtype=np.int8)
+        signs[0, _parse_positions(pos)] = 1
+        want = np.array([int(w, 16) for w in words.split()], dtype=np.uint32)
+        got = O.pack_signs_ref(signs)
+        assert got.shape == (1, want.size)
+        np.testing.assert_array_equal(got[0], want)
+        np.testing.assert_array_equal(O.signs_from_packed(got, K), signs)
+
+
+def _unpack_by_shifts(words, K):
+    rows = len(words)
+    out = np.zeros((rows, K), dtype=np.int8)
+    for i in range(rows):
+        for k in range(K):
+            out[i, k] = 1 if (int(words[i][k >> 5]) >> (k & 31)) & 1 else -1
+    return out
+
+
+def test_unpack_matches_shift_route():
+    """np.unpackbits route == pure-Python shift route on random words (ragged K)."""
+    rng = np.random.default_rng(5)
+    for K in (1, 31, 32, 33, 95, 160):
+        w = synth.random_sign_words(rng, 5, K, ldw=synth.words_per_row(K) + 1)
+        np.testing.assert_array_equal(O.signs_from_packed(w, K), _unpack_by_shifts(w, K))
+
+
+def test_pack_round_trip_and_zero_sign():
+    rng = np.random.default_rng(6)
+    sg = synth.random_signs_i8(rng, 7, 77)
+    p = O.pack_signs_ref(sg, ldw=4)
+    assert p.shape == (7, 4) and np.all(p[:, 3] == 0)
+    assert np.all((p[:, 2] >> np.uint32(77 - 64)) == 0)   # padding bits are 0
+    np.testing.assert_array_equal(O.signs_from_packed(p, 77), sg)
+    z = np.zeros((1, 40), dtype=np.int8)                  # sign 0 packs as a 0 bit
+    assert np.all(O.pack_signs_ref(z) == 0)
+
+
+# ----------------------------------------------------------------- worked example
+def _worked():
+    kv = {}
+    for ln in _lines("worked_lq2_1.txt"):
+        key, rest = ln.split(None, 1)
+        kv[key] = rest
+    D, d = int(kv["D"]), int(kv["d"])
+    M = np.array([[float(x) for x in kv["M"].split()]], dtype=np.float32)
+    words = np.array([[int(w, 16)] for w in kv["words"].split()], dtype=np.uint32)
+    T = np.array([[float(x) for x in r.split()] for r in kv["T"].split("|")])[None]
+    s = np.array([float(x) for x in kv["s"].split()], dtype=np.float32)
+    a = np.array([[float(x) for x in r.split()] for r in kv["a"].split("|")], dtype=np.float32)
+    o = np.array([[float(x) for x in r.split()] for r in kv["o"].split("|")])
+    ah = np.array([float(x) for x in kv["ahat0"].split()])
+    return D, d, M, words, T, s, a, o, ah
+
+
+def test_worked_example_all_routes():
+    """Hand-worked LQ-2/1 layer: every oracle route reproduces the outputs exactly."""
+    D, d, M, words, T, s, a, o, ah = _worked()
+    K = 4 // d * D
+    for f in (O.forward, O.forward_lifted, O.forward_loops):
+        np.testing.assert_array_equal(f(words, K, M, T, s, a, d, D, "f32"), o)
+    u = O.transform(a.astype(np.float64), T)
+    np.testing.assert_array_equal(O.lift(u, M, d, D)[0], ah)
+
+
+def test_worked_example_catches_slips():
+    """The worked example distinguishes the plausible wrong readings."""
+    D, d, M, words, T, s, a, o, ah = _worked()
+    K = 8
+    # transposed T^-1
+    wrong_t = O.forward(words, K, M, np.transpose(T, (0, 2, 1)).copy(), s, a, d, D, "f32")
+    assert not np.allclose(wrong_t, o)
+    # MSB-first bit order inside the byte
+    rev = np.array([[int(f"{int(w[0]):08b}"[::-1], 2)] for w in words], dtype=np.uint32)
+    assert not np.allclose(O.forward(rev, K, M, T, s, a, d, D, "f32"), o)
+    # group-major vs position-major lifted index (k = j*G + g)
+    y = O.signs_from_packed(words, K).reshape(2, 4, 2).transpose(0, 2, 1).reshape(2, 8)
+    alt = O.pack_signs_ref(y)
+    assert not np.allclose(O.forward(alt, K, M, T, s, a, d, D, "f32"), o)
+
+
+# ----------------------------------------------------------------- integer special case
+def _int_matvec_textbook(words, K, a_int):
+    """o = W_q a over the integers with +-1 entries from explicit bit tests."""
+    rows = words.shape[0]
+    out = np.zeros((a_int.shape[0], rows), dtype=np.int64)
+    kk = np.arange(K)
+    for i in range(rows):
+        bits = (words[i, kk >> 5].astype(np.int64) >> (kk & 31)) & 1
+        sig = 2 * bits - 1
+        out[:, i] = a_int.astype(np.int64) @ sig
+    return out
+
+
+def test_integer_special_case_exact():
+    """D = d, M = I, T^-1 = I, s = 1, integer a: o is the exact binary mat-vec."""
+    rng = np.random.default_rng(11)
+    d = D = 4
+    n = 256
+    m, B = 37, 3
+    L = synth.make_layer(m, n, d, D, B, seed=3, dtype="bf16", s_range=(1.0, 1.0), identity_t=True)
+    M = np.eye(d, dtype=np.float32)
+    a_int = rng.integers(-50, 51, size=(B, n)).astype(np.float32)
+    a = synth.to_storage(a_int, "bf16")          # small integers are exact in bf16
+    s = np.ones(m, dtype=np.float32)
+    got = O.forward(L.packed, n, M, L.t_inv, s, a, d, D, "bf16")
+    want = _int_matvec_textbook(L.packed, n, a_int)
+    np.testing.assert_array_equal(got, want.astype(np.float64))
+    # a = e_k picks out the signs of column k
+    e = np.zeros((1, n), dtype=np.float32)
+    e[0, 77] = 1
+    col = O.forward(L.packed, n, M, L.t_inv, s, synth.to_storage(e, "bf16"), d, D, "bf16")[0]
+    np.testing.assert_array_equal(col, O.signs_from_packed(L.packed, n)[:, 77])
+
+
+# ----------------------------------------------------------------- invariants
+def _tiny_layer(m=6, n=256, d=8, D=19, B=2, seed=9, dtype="bf16"):
+    return synth.make_layer(m, n, d, D, B, seed=seed, dtype=dtype)
+
+
+def test_all_plus_all_minus_closed_form():
+    """All bits 1: W_hat rows repeat rowsum(M); with T^-1 = I and a = 1,
+    o_i = s_i * (n/d) * sum(M).  All bits 0 negates it."""
+    d, D, n, m = 8, 19, 256, 5
+    L = synth.make_layer(m, n, d, D, 1, seed=4, identity_t=True)
+    K = L.K
+    ones = np.full_like(L.packed, 0xFFFFFFFF)
+    a = synth.to_storage(np.ones((1, n), np.float32), "bf16")
+    want = L.s.astype(np.float64) * (n // d) * L.M.astype(np.float64).sum()
+    got = O.forward(ones, K, L.M, L.t_inv, L.s, a, d, D, "bf16")[0]
+    np.testing.assert_allclose(got, want, rtol=1e-12)
+    zeros = np.zeros_like(L.packed)
+    np.testing.assert_allclose(O.forward(zeros, K, L.M, L.t_inv, L.s, a, d, D, "bf16")[0], -want,
+                               rtol=1e-12)
+
+
+def test_row_flip_negates_and_linearity():
+    L = _tiny_layer()
+    K = L.K
+    o = O.forward(L.packed, K, L.M, L.t_inv, L.s, L.a, L.d, L.D, L.dtype)
+    flipped = L.packed.copy()
+    flipped[2] = ~flipped[2]
+    o2 = O.forward(flipped, K, L.M, L.t_inv, L.s, L.a, L.d, L.D, L.dtype)
+    np.testing.assert_allclose(o2[:, 2], -o[:, 2], rtol=1e-12)
+    np.testing.assert_array_equal(np.delete(o2, 2, axis=1), np.delete(o, 2, axis=1))
+    # linear in a (float64 inputs) and in s
+    a64 = O.decode(L.a, L.dtype)
+    T64 = O.decode(L.t_inv, L.dtype)
+    f = lambda aa, ss: O.forward(L.packed, K, L.M, T64, ss, aa, L.d, L.D, "f64")
+    a2 = np.random.default_rng(1).standard_normal(a64.shape)
+    np.testing.assert_allclose(f(2 * a64 - 3 * a2, L.s), 2 * f(a64, L.s) - 3 * f(a2, L.s),
+                               rtol=1e-10, atol=1e-12)
+    s2 = np.arange(1, L.m + 1, dtype=np.float32)
+    np.testing.assert_allclose(f(a64, s2), f(a64, np.ones(L.m, np.float32)) * s2[None, :],
+                               rtol=1e-12)
+
+
+def test_transform_orthogonal_blocks_preserve_norm():
+    """u = T^-1 a with float64 Haar blocks keeps the norm of every 128-block."""
+    rng = np.random.default_rng(2)
+    T = np.stack([synth.haar_orthogonal(rng, 128) for _ in range(3)])
+    a = rng.standard_normal((4, 384))
+    u = O.transform(a, T)
+    np.testing.assert_allclose(np.linalg.norm(u.reshape(4, 3, 128), axis=2),
+                               np.linalg.norm(a.reshape(4, 3, 128), axis=2), rtol=1e-12)
+    # block orientation: a one-hot input picks out column c of its block only
+    e = np.zeros((1, 384))
+    e[0, 128 + 5] = 1
+    ue = O.transform(e, T)
+    np.testing.assert_array_equal(ue[0, :128], 0)
+    np.testing.assert_array_equal(ue[0, 256:], 0)
+    np.testing.assert_array_equal(ue[0, 128:256], T[1][:, 5])
+
+
+def test_routes_agree_against_brute_force():
+    """Vectorised reconstruct and lifted routes == pure-Python loops (tiny sizes)."""
+    for (m, n, d, D, B, dt) in [(3, 128, 8, 19, 2, "bf16"), (2, 256, 16, 40, 1, "bf16"),
+                                (3, 128, 8, 20, 1, "f16")]:
+        L = synth.make_layer(m, n, d, D, B, seed=m * 7 + D, dtype=dt)
+        ref = O.forward_loops(L.packed, L.K, L.M, L.t_inv, L.s, L.a, d, D, dt)
+        for f in (O.forward, O.forward_lifted):
+            got = f(L.packed, L.K, L.M, L.t_inv, L.s, L.a, d, D, dt)
+            np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-14 * np.abs(ref).max())
+
+
+def test_d10_groups_straddle_blocks():
+    """d = 10 does not divide 128: groups cross transform blocks; routes still agree."""
+    L = synth.make_layer(2, 640, 10, 24, 1, seed=21, dtype="f16")
+    ref = O.forward_loops(L.packed, L.K, L.M, L.t_inv, L.s, L.a, 10, 24, "f16")
+    np.testing.assert_allclose(O.forward(L.packed, L.K, L.M, L.t_inv, L.s, L.a, 10, 24, "f16"),
+                               ref, rtol=1e-12)
+
+
+def test_row_subset_equals_full():
+    L = _tiny_layer(m=40, B=3)
+    full = O.forward(L.packed, L.K, L.M, L.t_inv, L.s, L.a, L.d, L.D, L.dtype, chunk=7)
+    rows = [39, 0, 17, 17, 5]
+    sub = O.forward(L.packed, L.K, L.M, L.t_inv, L.s, L.a, L.d, L.D, L.dtype, rows=rows)
+    np.testing.assert_allclose(sub, full[:, rows], rtol=1e-13, atol=1e-15)
+
+
+def test_clt_statistics_sanity():
+    """M ~ N(0, 1/D) gives reconstructed weights of mean ~0 and variance ~1
+    (the central-limit codebook of the notes); a sanity check, not parity."""
+    rng = np.random.default_rng(8)
+    D, d = 19, 8
+    M = (rng.standard_normal((d, D)) / np.sqrt(D))
+    y = O.signs_from_packed(synth.random_sign_words(rng, 2000, 64 * D), 64 * D)
+    w = O.reconstruct_weights(y, M, d, D)
+    assert abs(w.mean()) < 0.02
+    np.testing.assert_allclose(w.var(), (M ** 2).sum(axis=1).mean(), rtol=0.02)
+    assert 0.6 < w.var() < 1.4
+
+
+# ----------------------------------------------------------------- storage decode
+def test_bf16_decode_and_rounding():
+    x = np.array([1.0, -2.5, 3.140625, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 65504.0], np.float32)
+    b = synth.to_bf16_bits(x)
+    # 1+2^-8 is a tie -> rounds to even (1.0); 1+3*2^-8 -> 1+2^-6 (ties to even)
+    np.testing.assert_array_equal(O.decode(b, "bf16"),
+                                  [1.0, -2.5, 3.140625, 1.0, 1.0 + 2 ** -6, 65536.0])
+    assert b[0] == 0x3F80 and b[1] == 0xC020
+
+
+def test_error_metric():
+    ref = np.array([[1.0, -4.0, 2.0], [0.0, 0.0, 0.5]])
+    got = ref + np.array([[0.0, 0.004, -0.002], [0.001, 0.0, 0.0]])
+    assert O.rel_err_colmax(got, ref) == pytest.approx(max(0.004 / 4.0, 0.001 / 0.5))
