@@ -1,0 +1,182 @@
+// C ABI of liblq: host-side validation and dispatch (declarations in include/lq.h).
+// Every entry point checks its arguments before launching anything, returns a
+// status code and records a thread-local message on failure.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "lq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+lq_status fail(lq_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+lq_status ok() {
+  g_err[0] = '\0';
+  return LQ_OK;
+}
+
+lq_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(LQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+bool valid_dtype(lq_dtype dt) { return dt == LQ_F32 || dt == LQ_F16 || dt == LQ_BF16; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+size_t dtype_size(lq_dtype dt) { return dt == LQ_F32 ? 4 : 2; }
+
+}  // namespace
+
+extern "C" {
+
+const char* lq_status_string(lq_status st) {
+  switch (st) {
+    case LQ_OK: return "LQ_OK";
+    case LQ_ERR_NULL: return "LQ_ERR_NULL";
+    case LQ_ERR_SHAPE: return "LQ_ERR_SHAPE";
+    case LQ_ERR_DTYPE: return "LQ_ERR_DTYPE";
+    case LQ_ERR_ALIGN: return "LQ_ERR_ALIGN";
+    case LQ_ERR_UNSUPPORTED: return "LQ_ERR_UNSUPPORTED";
+    case LQ_ERR_HIP: return "LQ_ERR_HIP";
+    case LQ_ERR_WORKSPACE: return "LQ_ERR_WORKSPACE";
+    default: return "LQ_ERR_UNKNOWN";
+  }
+}
+
+const char* lq_last_error(void) { return g_err; }
+
+const char* lq_version(void) { return "liblq 0.1 gfx950"; }
+
+lq_status lq_pack_signs(const int8_t* signs, int64_t rows, int64_t K, int64_t lds,
+                        uint32_t* packed, int64_t ldw, void* stream) {
+  if (rows < 0 || K < 0 || ldw < 0 || lds < 0)
+    return fail(LQ_ERR_SHAPE, "negative size (rows=%lld K=%lld lds=%lld ldw=%lld)",
+                (long long)rows, (long long)K, (long long)lds, (long long)ldw);
+  if (ldw < (K + 31) / 32) return fail(LQ_ERR_SHAPE, "ldw=%lld < ceil(K/32)", (long long)ldw);
+  if (lds < K) return fail(LQ_ERR_SHAPE, "lds=%lld < K=%lld", (long long)lds, (long long)K);
+  if (rows == 0 || ldw == 0) return ok();
+  if (!packed || (K > 0 && !signs)) return fail(LQ_ERR_NULL, "null pointer");
+  if (!aligned(packed, 4)) return fail(LQ_ERR_ALIGN, "packed must be 4-byte aligned");
+  return hip_status(lq::launch_pack_signs(signs, rows, K, lds, packed, ldw, as_stream(stream)),
+                    "lq_pack_signs launch");
+}
+
+lq_status lq_unpack_signs(const uint32_t* packed, int64_t rows, int64_t K, int64_t ldw,
+                          int8_t* signs, int64_t lds, void* stream) {
+  if (rows < 0 || K < 0 || ldw < 0 || lds < 0) return fail(LQ_ERR_SHAPE, "negative size");
+  if (ldw < (K + 31) / 32) return fail(LQ_ERR_SHAPE, "ldw=%lld < ceil(K/32)", (long long)ldw);
+  if (lds < K) return fail(LQ_ERR_SHAPE, "lds=%lld < K=%lld", (long long)lds, (long long)K);
+  if (rows == 0 || K == 0) return ok();
+  if (!packed || !signs) return fail(LQ_ERR_NULL, "null pointer");
+  if (!aligned(packed, 4)) return fail(LQ_ERR_ALIGN, "packed must be 4-byte aligned");
+  return hip_status(lq::launch_unpack_signs(packed, rows, K, ldw, signs, lds, as_stream(stream)),
+                    "lq_unpack_signs launch");
+}
+
+lq_status lq_lift_activations(const void* a, lq_dtype a_dtype, int64_t B, int64_t n,
+                              const void* t_inv, lq_dtype t_dtype, int32_t t_block,
+                              const float* M, int32_t d, int32_t D, void* a_lift,
+                              lq_dtype lift_dtype, void* stream) {
+  if (!a || !t_inv || !M || !a_lift) return fail(LQ_ERR_NULL, "null pointer");
+  if (!valid_dtype(a_dtype) || !valid_dtype(t_dtype) || !valid_dtype(lift_dtype))
+    return fail(LQ_ERR_DTYPE, "unknown dtype");
+  if (t_block != 128)
+    return fail(LQ_ERR_UNSUPPORTED, "t_block=%d (only 128 is implemented)", (int)t_block);
+  if (B < 1 || n < 1) return fail(LQ_ERR_SHAPE, "B=%lld n=%lld", (long long)B, (long long)n);
+  if (d < 1 || d > 64 || D < 1 || D > 256 || d * D > 8192)
+    return fail(LQ_ERR_SHAPE, "d=%d D=%d out of range (1..64, 1..256, d*D <= 8192)", (int)d,
+                (int)D);
+  if (n % 128) return fail(LQ_ERR_SHAPE, "n=%lld not a multiple of t_block", (long long)n);
+  if (n % d) return fail(LQ_ERR_SHAPE, "n=%lld not a multiple of d=%d", (long long)n, (int)d);
+  if ((int64_t)n / d * D > INT32_MAX || n > INT32_MAX || B > INT32_MAX / 2)
+    return fail(LQ_ERR_SHAPE, "sizes exceed 32-bit indexing");
+  if (!aligned(t_inv, 16)) return fail(LQ_ERR_ALIGN, "t_inv must be 16-byte aligned");
+  if (!aligned(a, dtype_size(a_dtype)) || !aligned(a_lift, dtype_size(lift_dtype)) ||
+      !aligned(M, 4))
+    return fail(LQ_ERR_ALIGN, "misaligned pointer");
+  return hip_status(lq::launch_lift(a, a_dtype, B, n, t_inv, t_dtype, M, d, D, a_lift, lift_dtype,
+                                    as_stream(stream)),
+                    "lq_lift_activations launch");
+}
+
+lq_status lq_gemv_workspace_size(int64_t m, int64_t K, int64_t B, size_t* bytes) {
+  if (!bytes) return fail(LQ_ERR_NULL, "bytes is null");
+  if (m < 1 || K < 1 || B < 1 || B > 16)
+    return fail(LQ_ERR_SHAPE, "m=%lld K=%lld B=%lld", (long long)m, (long long)K, (long long)B);
+  *bytes = lq::gemv_workspace_bytes(m, K, B);
+  return ok();
+}
+
+lq_status lq_workspace_clear(void* workspace, size_t bytes, void* stream) {
+  if (bytes == 0) return ok();
+  if (!workspace) return fail(LQ_ERR_NULL, "workspace is null");
+  if (!aligned(workspace, 16)) return fail(LQ_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return hip_status(lq::launch_fill_zero(workspace, bytes, as_stream(stream)),
+                    "lq_workspace_clear launch");
+}
+
+lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw, const float* s,
+                  const float* a_lift, int64_t B, float* out, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  if (!w_packed || !s || !a_lift || !out) return fail(LQ_ERR_NULL, "null pointer");
+  if (m < 1 || K < 1) return fail(LQ_ERR_SHAPE, "m=%lld K=%lld", (long long)m, (long long)K);
+  if (B < 1 || B > 16) return fail(LQ_ERR_SHAPE, "B=%lld outside 1..16", (long long)B);
+  if (ldw < (K + 31) / 32) return fail(LQ_ERR_SHAPE, "ldw=%lld < ceil(K/32)", (long long)ldw);
+  if (ldw % 2) return fail(LQ_ERR_ALIGN, "ldw=%lld must be even", (long long)ldw);
+  if (K % 4) return fail(LQ_ERR_SHAPE, "K=%lld must be a multiple of 4", (long long)K);
+  if (m * ldw * 4 > (int64_t)UINT32_MAX)
+    return fail(LQ_ERR_SHAPE, "weights of %lld bytes exceed the 4 GiB per-call limit",
+                (long long)(m * ldw * 4));
+  if (!aligned(w_packed, 8)) return fail(LQ_ERR_ALIGN, "w_packed must be 8-byte aligned");
+  if (!aligned(a_lift, 16)) return fail(LQ_ERR_ALIGN, "a_lift must be 16-byte aligned");
+  if (!aligned(s, 4) || !aligned(out, 4)) return fail(LQ_ERR_ALIGN, "misaligned s or out");
+  const size_t need = lq::gemv_workspace_bytes(m, K, B);
+  if (need > 0) {
+    if (!workspace) return fail(LQ_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if (workspace_bytes < need)
+      return fail(LQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    if (!aligned(workspace, 256)) return fail(LQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+  }
+  // Tokens go through in groups of at most 4; each group rereads the weights.
+  for (int64_t t0 = 0; t0 < B; t0 += 4) {
+    const int64_t bt = (B - t0) < 4 ? (B - t0) : 4;
+    const lq::GemvPlan pl = lq::plan_gemv(m, K, bt);
+    const hipError_t e = lq::launch_gemv(pl, w_packed, m, K, ldw, s, a_lift + t0 * K, bt,
+                                         out + t0 * m, workspace, as_stream(stream));
+    if (e != hipSuccess) return hip_status(e, "lq_gemv launch");
+  }
+  return ok();
+}
+
+lq_status lq_gemm(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw, const float* s,
+                  const void* a_lift, lq_dtype lift_dtype, int64_t B, float* out, void* stream) {
+  if (!w_packed || !s || !a_lift || !out) return fail(LQ_ERR_NULL, "null pointer");
+  if (lift_dtype != LQ_F16 && lift_dtype != LQ_BF16)
+    return fail(LQ_ERR_DTYPE, "lq_gemm takes LQ_F16 or LQ_BF16 lifted activations");
+  if (m < 1 || K < 1 || B < 1)
+    return fail(LQ_ERR_SHAPE, "m=%lld K=%lld B=%lld", (long long)m, (long long)K, (long long)B);
+  if (ldw < (K + 31) / 32) return fail(LQ_ERR_SHAPE, "ldw=%lld < ceil(K/32)", (long long)ldw);
+  if (K % 8) return fail(LQ_ERR_SHAPE, "K=%lld must be a multiple of 8", (long long)K);
+  if (m > INT32_MAX || B > INT32_MAX || K > INT32_MAX)
+    return fail(LQ_ERR_SHAPE, "sizes out of range");
+  if (!aligned(w_packed, 4)) return fail(LQ_ERR_ALIGN, "w_packed must be 4-byte aligned");
+  if (!aligned(a_lift, 16)) return fail(LQ_ERR_ALIGN, "a_lift must be 16-byte aligned");
+  if (!aligned(s, 4) || !aligned(out, 4)) return fail(LQ_ERR_ALIGN, "misaligned s or out");
+  return hip_status(lq::launch_gemm(w_packed, m, K, ldw, s, a_lift, lift_dtype, B, out,
+                                    as_stream(stream)),
+                    "lq_gemm launch");
+}
+
+}  // extern "C"

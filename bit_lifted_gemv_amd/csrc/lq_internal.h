@@ -1,0 +1,102 @@
+// Internal declarations shared by the HIP translation units of liblq.
+// Kernel launchers return hipError_t from the launch; argument validation
+// happens in lq_api.hip before any of them is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/lq.h"
+
+namespace lq {
+
+// ---------------------------------------------------------------- dtype helpers
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+__device__ __forceinline__ uint16_t float_to_bf16_bits_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float f16_bits_to_float(uint16_t b) {
+  _Float16 h;
+  __builtin_memcpy(&h, &b, 2);
+  return static_cast<float>(h);
+}
+
+__device__ __forceinline__ uint16_t float_to_f16_bits_rne(float f) {
+  _Float16 h = static_cast<_Float16>(f);   // v_cvt_f16_f32: round to nearest even
+  uint16_t b;
+  __builtin_memcpy(&b, &h, 2);
+  return b;
+}
+
+// Load element i of a typed 16/32-bit array as float.
+template <int DT>
+__device__ __forceinline__ float load_as_float(const void* p, int64_t i);
+
+template <>
+__device__ __forceinline__ float load_as_float<LQ_F32>(const void* p, int64_t i) {
+  return static_cast<const float*>(p)[i];
+}
+template <>
+__device__ __forceinline__ float load_as_float<LQ_F16>(const void* p, int64_t i) {
+  return f16_bits_to_float(static_cast<const uint16_t*>(p)[i]);
+}
+template <>
+__device__ __forceinline__ float load_as_float<LQ_BF16>(const void* p, int64_t i) {
+  return bf16_bits_to_float(static_cast<const uint16_t*>(p)[i]);
+}
+
+template <int DT>
+__device__ __forceinline__ void store_from_float(void* p, int64_t i, float v);
+
+template <>
+__device__ __forceinline__ void store_from_float<LQ_F32>(void* p, int64_t i, float v) {
+  static_cast<float*>(p)[i] = v;
+}
+template <>
+__device__ __forceinline__ void store_from_float<LQ_F16>(void* p, int64_t i, float v) {
+  static_cast<uint16_t*>(p)[i] = float_to_f16_bits_rne(v);
+}
+template <>
+__device__ __forceinline__ void store_from_float<LQ_BF16>(void* p, int64_t i, float v) {
+  static_cast<uint16_t*>(p)[i] = float_to_bf16_bits_rne(v);
+}
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_pack_signs(const int8_t* signs, int64_t rows, int64_t K, int64_t lds,
+                             uint32_t* packed, int64_t ldw, hipStream_t st);
+hipError_t launch_unpack_signs(const uint32_t* packed, int64_t rows, int64_t K, int64_t ldw,
+                               int8_t* signs, int64_t lds, hipStream_t st);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
+
+hipError_t launch_lift(const void* a, lq_dtype a_dt, int64_t B, int64_t n, const void* t_inv,
+                       lq_dtype t_dt, const float* M, int d, int D, void* out, lq_dtype out_dt,
+                       hipStream_t st);
+
+// GEMV plan: how the rows and the lifted dimension are split over workgroups.
+struct GemvPlan {
+  int rows_per_wg;      // multiple of 64
+  int slices_per_part;  // 512-bit slices handled by one workgroup
+  int parts;            // number of K-parts (split-K factor)
+  int row_blocks;
+  int slices;           // ceil(K / 512)
+  size_t ws_bytes;      // partial sums + arrival counters (0 when parts == 1)
+};
+GemvPlan plan_gemv(int64_t m, int64_t K, int64_t B);
+size_t gemv_counter_bytes(int64_t m);
+// Workspace bytes of lq_gemv for B tokens (they go through in groups of <= 4).
+size_t gemv_workspace_bytes(int64_t m, int64_t K, int64_t B);
+hipError_t launch_gemv(const GemvPlan& plan, const uint32_t* w, int64_t m, int64_t K,
+                       int64_t ldw, const float* s, const float* a_lift, int64_t B, float* out,
+                       void* ws, hipStream_t st);
+
+hipError_t launch_gemm(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
+                       const void* a_lift, lq_dtype dt, int64_t B, float* out, hipStream_t st);
+
+}  // namespace lq

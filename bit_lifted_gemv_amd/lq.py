@@ -1,0 +1,237 @@
+"""ctypes binding of liblq (include/lq.h): argument marshalling only.
+
+Every function here passes device pointers, sizes and the current HIP stream
+of torch to the C ABI; all arithmetic of the layer runs in the library's HIP
+kernels.  Importing this module opens ``liblq.so`` next to it and raises if
+the library is missing -- there is no fallback.
+
+Packed weights are held in torch.int32 tensors (the same 32 bits as the ABI's
+uint32 words).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblq.so")
+
+LQ_F32, LQ_F16, LQ_BF16 = 0, 1, 2
+STATUS = {0: "LQ_OK", 1: "LQ_ERR_NULL", 2: "LQ_ERR_SHAPE", 3: "LQ_ERR_DTYPE", 4: "LQ_ERR_ALIGN",
+          5: "LQ_ERR_UNSUPPORTED", 6: "LQ_ERR_HIP", 7: "LQ_ERR_WORKSPACE"}
+
+EXPORTS = ("lq_status_string", "lq_last_error", "lq_version", "lq_pack_signs", "lq_unpack_signs",
+           "lq_lift_activations", "lq_gemv_workspace_size", "lq_workspace_clear", "lq_gemv",
+           "lq_gemm")
+
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+
+class LQError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m bit_lifted_gemv_amd.build`")
+    lib = ctypes.CDLL(path)
+    sig = {
+        "lq_status_string": (ctypes.c_char_p, [_i32]),
+        "lq_last_error": (ctypes.c_char_p, []),
+        "lq_version": (ctypes.c_char_p, []),
+        "lq_pack_signs": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp]),
+        "lq_unpack_signs": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp]),
+        "lq_lift_activations": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _i32, _vp, _i32, _i32,
+                                       _vp, _i32, _vp]),
+        "lq_gemv_workspace_size": (_i32, [_i64, _i64, _i64, ctypes.POINTER(_sz)]),
+        "lq_workspace_clear": (_i32, [_vp, _sz, _vp]),
+        "lq_gemv": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
+        "lq_gemm": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _i32, _i64, _vp, _vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_LIB: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    global _LIB
+    if _LIB is None:
+        _LIB = load_library()
+    return _LIB
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise LQError(status, lib().lq_last_error().decode())
+
+
+# ----------------------------------------------------------------- helpers
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return LQ_F32
+    if t.dtype == torch.float16:
+        return LQ_F16
+    if t.dtype == torch.bfloat16:
+        return LQ_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _torch_dt(code: int) -> torch.dtype:
+    return {LQ_F32: torch.float32, LQ_F16: torch.float16, LQ_BF16: torch.bfloat16}[code]
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(*ts: torch.Tensor) -> None:
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+# ----------------------------------------------------------------- C ABI wrappers
+def pack_signs(signs: torch.Tensor, ldw: Optional[int] = None, stream=None) -> torch.Tensor:
+    """int8 signs [rows][K] -> int32 words [rows][ldw] (LSB-first, bit 1 = positive)."""
+    _dev(signs)
+    rows, K = signs.shape
+    ldw = (K + 31) // 32 if ldw is None else ldw
+    out = torch.empty((rows, ldw), dtype=torch.int32, device=signs.device)
+    check(lib().lq_pack_signs(_ptr(signs), rows, K, K, _ptr(out), ldw, _stream(stream)))
+    return out
+
+
+def unpack_signs(packed: torch.Tensor, K: int, stream=None) -> torch.Tensor:
+    _dev(packed)
+    rows, ldw = packed.shape
+    out = torch.empty((rows, K), dtype=torch.int8, device=packed.device)
+    check(lib().lq_unpack_signs(_ptr(packed), rows, K, ldw, _ptr(out), K, _stream(stream)))
+    return out
+
+
+def lift(a: torch.Tensor, t_inv: torch.Tensor, M: torch.Tensor, d: int, D: int,
+         out_dtype: torch.dtype = torch.float32, t_block: int = 128,
+         out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """a [B][n], t_inv [n/128][128][128], M float [d][D] -> a_lift [B][n*D/d]."""
+    _dev(a, t_inv, M)
+    B, n = a.shape
+    K = n // d * D
+    if out is None:
+        out = torch.empty((B, K), dtype=out_dtype, device=a.device)
+    check(lib().lq_lift_activations(_ptr(a), _dt(a), B, n, _ptr(t_inv), _dt(t_inv), t_block,
+                                    _ptr(M), d, D, _ptr(out), _dt(out), _stream(stream)))
+    return out
+
+
+_WS = {}
+
+
+def workspace(nbytes: int, device: torch.device) -> torch.Tensor:
+    """A zeroed workspace of at least nbytes, cached per device (grown on demand)."""
+    key = (device.type, device.index)
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _WS[key] = ws
+    return ws
+
+
+def gemv_workspace_size(m: int, K: int, B: int) -> int:
+    n = _sz(0)
+    check(lib().lq_gemv_workspace_size(m, K, B, ctypes.byref(n)))
+    return n.value
+
+
+def gemv(w_packed: torch.Tensor, s: torch.Tensor, a_lift: torch.Tensor, K: Optional[int] = None,
+         out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out [B][m] = s * (sigma @ a_lift^T), float32 lifted activations, 1 <= B <= 16."""
+    _dev(w_packed, s, a_lift)
+    m, ldw = w_packed.shape
+    B, Ka = a_lift.shape
+    K = Ka if K is None else K
+    if out is None:
+        out = torch.empty((B, m), dtype=torch.float32, device=a_lift.device)
+    nws = gemv_workspace_size(m, K, B)
+    ws = workspace(nws, a_lift.device) if nws else None
+    check(lib().lq_gemv(_ptr(w_packed), m, K, ldw, _ptr(s), _ptr(a_lift), B, _ptr(out), _ptr(ws),
+                        nws, _stream(stream)))
+    return out
+
+
+def gemm(w_packed: torch.Tensor, s: torch.Tensor, a_lift: torch.Tensor, K: Optional[int] = None,
+         out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out [B][m] on the matrix cores; a_lift float16 or bfloat16 [B][K]."""
+    _dev(w_packed, s, a_lift)
+    m, ldw = w_packed.shape
+    B, Ka = a_lift.shape
+    K = Ka if K is None else K
+    if out is None:
+        out = torch.empty((B, m), dtype=torch.float32, device=a_lift.device)
+    check(lib().lq_gemm(_ptr(w_packed), m, K, ldw, _ptr(s), _ptr(a_lift), _dt(a_lift), B,
+                        _ptr(out), _stream(stream)))
+    return out
+
+
+# ----------------------------------------------------------------- layer
+class DeviceLayer:
+    """A layer's stored arrays resident on the GPU (uploaded once)."""
+
+    def __init__(self, packed, M, t_inv, s, d: int, D: int, n: int, act_dtype: str,
+                 device="cuda"):
+        import numpy as np
+        self.d, self.D, self.n = d, D, n
+        self.K = n // d * D
+        self.m = packed.shape[0]
+        self.act_dtype = act_dtype
+        self.w = torch.from_numpy(np.ascontiguousarray(packed).view(np.int32)).to(device)
+        self.M = torch.from_numpy(np.ascontiguousarray(M, dtype=np.float32)).to(device)
+        self.t_inv = to_torch_16(t_inv, act_dtype).to(device)
+        self.s = torch.from_numpy(np.ascontiguousarray(s, dtype=np.float32)).to(device)
+
+    @classmethod
+    def from_synth(cls, L, device="cuda") -> "DeviceLayer":
+        return cls(L.packed, L.M, L.t_inv, L.s, L.d, L.D, L.n, L.dtype, device)
+
+    def forward(self, a: torch.Tensor, gemm_dtype: torch.dtype = torch.float16,
+                path: str = "auto") -> torch.Tensor:
+        """o [B][m]: lift then the GEMV (B <= 16) or the GEMM (larger B)."""
+        B = a.shape[0]
+        use_gemm = path == "gemm" or (path == "auto" and B > 16)
+        if use_gemm:
+            al = lift(a, self.t_inv, self.M, self.d, self.D, out_dtype=gemm_dtype)
+            return gemm(self.w, self.s, al, self.K)
+        al = lift(a, self.t_inv, self.M, self.d, self.D, out_dtype=torch.float32)
+        return gemv(self.w, self.s, al, self.K)
+
+
+def to_torch_16(x, dtype: str) -> torch.Tensor:
+    """Host array in storage format (float16, or bf16 bits as uint16) -> torch CPU tensor."""
+    import numpy as np
+    x = np.ascontiguousarray(x)
+    if dtype == "f16":
+        return torch.from_numpy(x.astype(np.float16))
+    if dtype == "bf16":
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16)
+    if dtype == "f32":
+        return torch.from_numpy(x.astype(np.float32))
+    raise ValueError(dtype)

@@ -1,0 +1,157 @@
+/*
+ * lq.h -- C ABI of the LiftQuant lift-then-project linear layer on MI355X.
+ *
+ * The layer (LiftQuant notes, "LiftQuant: Continuous Bit-Width LLM via
+ * Dimensional Lifting and Projection", section 关键设计 4 and the 推理 node of
+ * the 整体框架 flowchart) is
+ *
+ *     o = diag(s) . W_q . lift(T^-1 a)
+ *
+ *   * W_q in {+-1}^(m x K) holds one sign per bit (关键设计 1: a d-wide weight
+ *     group is w = M y with y in {+-1}^D, so K = n*D/d and the bit-width is D/d);
+ *   * T^-1 is a per-layer transform, here block-diagonal with square blocks;
+ *   * lift applies M^T (M is d x D) to every d-wide group of u = T^-1 a:
+ *     a_hat[g*D + j] = sum_r M[r][j] u[g*d + r].  Since y.(M^T u_g) = (M y).u_g
+ *     this equals the product with the reconstructed weights;
+ *   * s is a per-output-row scale (the notes write diag(s) and nothing more).
+ * The notes split the run-time work into one small transform of the
+ * activations and then the product of the 1-bit weights with the result
+ * (关键设计 4); the calls below are those two steps.
+ *
+ * Conventions (all calls):
+ *   - Every pointer except host-side size outputs is a DEVICE pointer owned by
+ *     the caller.  The library keeps no buffers of its own.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  A
+ *     call validates its arguments on the host, enqueues its kernels on
+ *     `stream` and returns without synchronising.
+ *   - On any validation failure the call returns a nonzero lq_status, sets a
+ *     thread-local message (lq_last_error) and launches nothing.  A failed
+ *     launch returns LQ_ERR_HIP.
+ *   - Outputs must not alias inputs.  All arrays are row-major and dense in
+ *     their last dimension; leading dimensions are given where they may differ.
+ *   - Calls are thread-safe; calls that share a workspace must not overlap.
+ */
+#ifndef LQ_H_
+#define LQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t lq_status;
+#define LQ_OK              0
+#define LQ_ERR_NULL        1  /* a required pointer is NULL                        */
+#define LQ_ERR_SHAPE       2  /* sizes inconsistent or out of range                */
+#define LQ_ERR_DTYPE       3  /* unsupported element type for this argument        */
+#define LQ_ERR_ALIGN       4  /* a pointer or leading dimension is misaligned      */
+#define LQ_ERR_UNSUPPORTED 5  /* valid request this build does not implement        */
+#define LQ_ERR_HIP         6  /* the HIP runtime reported an error                  */
+#define LQ_ERR_WORKSPACE   7  /* workspace missing or too small                     */
+
+typedef int32_t lq_dtype;
+#define LQ_F32  0
+#define LQ_F16  1
+#define LQ_BF16 2
+
+/* Human-readable name of a status code (static string). */
+const char* lq_status_string(lq_status st);
+/* Message of the last failed call on this thread ("" if none). */
+const char* lq_last_error(void);
+/* Library version string. */
+const char* lq_version(void);
+
+/*
+ * lq_pack_signs -- pack signs into W_q words.
+ * Storage of W_q (关键设计 1: one bit per lifted sign, D signs per d weights):
+ *   packed: uint32 [rows][ldw]; lifted position k of a row is bit (k & 31) of
+ *   word (k >> 5); the bit is 1 iff signs[row][k] > 0 (0 and negatives pack as
+ *   0, i.e. -1).  Bits at positions >= K and words >= ceil(K/32) are written 0.
+ * signs:  int8 [rows][lds], lds >= K.
+ * Requires rows >= 0, K >= 0, ldw >= ceil(K/32), lds >= K; rows == 0 or
+ * K == 0 with ldw == 0 is a no-op.
+ */
+lq_status lq_pack_signs(const int8_t* signs, int64_t rows, int64_t K, int64_t lds,
+                        uint32_t* packed, int64_t ldw, void* stream);
+
+/*
+ * lq_unpack_signs -- inverse of lq_pack_signs: signs[row][k] = +1 if the bit
+ * is 1 else -1, for k < K (columns K..lds-1 are not written).
+ */
+lq_status lq_unpack_signs(const uint32_t* packed, int64_t rows, int64_t K, int64_t ldw,
+                          int8_t* signs, int64_t lds, void* stream);
+
+/*
+ * lq_lift_activations -- the small transform of the activations
+ * (关键设计 4, T* a, with T* read as T^-1 followed by M^T per group).
+ *   u[b][tb*q + r] = sum_c T_q[r][c] * a[b][tb*q + c]      (block q of T^-1)
+ *   a_lift[b][g*D + j] = sum_{r<d} M[r][j] * u[b][g*d + r]
+ * a:      [B][n] of a_dtype (LQ_F16 | LQ_BF16 | LQ_F32)
+ * t_inv:  [n/t_block][t_block][t_block] of t_dtype (LQ_F16 | LQ_BF16 | LQ_F32)
+ * M:      float [d][D]
+ * a_lift: [B][K] of lift_dtype, K = n*D/d.  LQ_F32 feeds lq_gemv; LQ_F16 or
+ *         LQ_BF16 (round to nearest even) feed lq_gemm.
+ * Accumulation is float32.  Requires t_block == 128, n % 128 == 0,
+ * n % d == 0, 1 <= d <= 64, 1 <= D <= 256, d*D <= 8192, B >= 1.
+ */
+lq_status lq_lift_activations(const void* a, lq_dtype a_dtype, int64_t B, int64_t n,
+                              const void* t_inv, lq_dtype t_dtype, int32_t t_block,
+                              const float* M, int32_t d, int32_t D,
+                              void* a_lift, lq_dtype lift_dtype, void* stream);
+
+/*
+ * lq_gemv_workspace_size -- bytes of workspace lq_gemv needs for this shape
+ * (0 when none).  Written to *bytes.
+ */
+lq_status lq_gemv_workspace_size(int64_t m, int64_t K, int64_t B, size_t* bytes);
+
+/*
+ * lq_workspace_clear -- zero `bytes` bytes of a workspace on `stream` with a
+ * fill kernel.  A new workspace must be cleared once before its first use;
+ * every completed lq_gemv call leaves it cleared again.
+ */
+lq_status lq_workspace_clear(void* workspace, size_t bytes, void* stream);
+
+/*
+ * lq_gemv -- the product of the 1-bit weights with the float lifted
+ * activations for small batches (关键设计 4 calls this the main body: an
+ * ordinary GEMM between 1-bit weights and floats, with no weight codebook to
+ * look up).  The kernel does keep lookup tables, but of activation sums built
+ * per call from a_lift, not of weights:
+ *   out[b][i] = s[i] * sum_{k<K} sigma_ik * a_lift[b][k],
+ *   sigma_ik = +1 if bit k of row i is 1, else -1.
+ * w_packed: uint32 [m][ldw] (layout of lq_pack_signs), ldw >= ceil(K/32),
+ *           ldw even and w_packed 8-byte aligned.
+ * s:        float [m].
+ * a_lift:   float [B][K] (lq_lift_activations with LQ_F32), 16-byte aligned,
+ *           K % 4 == 0.
+ * out:      float [B][m].
+ * workspace: device buffer of >= lq_gemv_workspace_size bytes, cleared once
+ *           (lq_workspace_clear); may be NULL when that size is 0.
+ * Requires 1 <= B <= 16, m >= 1, K >= 1.  Accumulation is float32; the
+ * result does not depend on the launch configuration's timing (no float
+ * atomics).
+ */
+lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw,
+                  const float* s, const float* a_lift, int64_t B, float* out,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lq_gemm -- the same product for large batches, contracted on the matrix
+ * cores: out[b][i] = s[i] * sum_k sigma_ik * a_lift[b][k] with a_lift in
+ * 16-bit (LQ_F16 or LQ_BF16) [B][K]; signs are expanded to exact +-1 16-bit
+ * tiles and multiplied with float32 accumulation.
+ * w_packed: as for lq_gemv; a_lift 16-byte aligned, K % 8 == 0.
+ * out: float [B][m].  Requires B >= 1, m >= 1, K >= 1.
+ */
+lq_status lq_gemm(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw,
+                  const float* s, const void* a_lift, lq_dtype lift_dtype, int64_t B,
+                  float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LQ_H_ */

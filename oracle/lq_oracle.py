@@ -33,7 +33,8 @@ import numpy as np
 
 __all__ = [
     "decode", "unpack_bits", "signs_from_packed", "pack_signs_ref", "reconstruct_weights",
-    "transform", "lift", "forward", "forward_lifted", "forward_loops", "rel_err_colmax",
+    "transform", "lift", "lifted_product", "forward", "forward_lifted", "forward_loops",
+    "rel_err_colmax",
 ]
 
 
@@ -130,15 +131,23 @@ def forward(packed: np.ndarray, K: int, M: np.ndarray, t_inv: np.ndarray, s: np.
     return out
 
 
+def lifted_product(packed: np.ndarray, K: int, a_lift: np.ndarray, s: np.ndarray,
+                   rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """o[b, i] = s_i * sum_k sigma_ik a_lift[b, k]  (sigma from the sign bits),
+    the contraction that follows the lift, for given lifted activations."""
+    al = np.asarray(a_lift, dtype=np.float64)
+    idx = np.arange(packed.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    y = signs_from_packed(packed[idx], K).astype(np.float64)
+    return (y @ al.T).T * np.asarray(s, dtype=np.float64)[idx][None, :]
+
+
 def forward_lifted(packed: np.ndarray, K: int, M: np.ndarray, t_inv: np.ndarray, s: np.ndarray,
                    a: np.ndarray, d: int, D: int, dtype: str,
                    rows: Optional[Sequence[int]] = None) -> np.ndarray:
     """o by the lifted route: a_hat = lift(T^-1 a), o = s * (Y a_hat)."""
     M64, T64, s64, a64 = _inputs64(M, t_inv, s, a, dtype)
     ah = lift(transform(a64, T64), M64, d, D)     # [B][K]
-    idx = np.arange(packed.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
-    y = signs_from_packed(packed[idx], K).astype(np.float64)
-    return (y @ ah.T).T * s64[idx][None, :]
+    return lifted_product(packed, K, ah, s64, rows)
 
 
 def forward_loops(packed, K, M, t_inv, s, a, d, D, dtype):

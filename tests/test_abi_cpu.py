@@ -1,0 +1,127 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_lifted_gemv_amd import lq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lq.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(lq_[a-z0-9_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    return lq.load_library()
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(lq.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    for code, name in lq.STATUS.items():
+        assert L.lq_status_string(code).decode() == name
+    assert L.lq_status_string(99).decode() == "LQ_ERR_UNKNOWN"
+    assert b"gfx950" in L.lq_version()
+
+
+# Fake, never-dereferenced device addresses: every call below must fail in
+# host-side validation, before any HIP call.
+P = 0x10000000
+MIS = 0x10000002
+
+
+def _err(L):
+    return L.lq_last_error().decode()
+
+
+def test_gemv_validation(L):
+    ws = 0
+    assert L.lq_gemv(None, 8, 64, 2, P, P, 1, P, None, ws, None) == 1       # null weights
+    assert L.lq_gemv(P, 8, 64, 2, P, P, 0, P, None, ws, None) == 2          # B = 0
+    assert L.lq_gemv(P, 8, 64, 2, P, P, 17, P, None, ws, None) == 2         # B > 16
+    assert "1..16" in _err(L)
+    assert L.lq_gemv(P, 8, 64, 1, P, P, 1, P, None, ws, None) == 2          # ldw < K/32
+    assert L.lq_gemv(P, 8, 96, 3, P, P, 1, P, None, ws, None) == 4          # odd ldw
+    assert L.lq_gemv(P, 8, 66, 4, P, P, 1, P, None, ws, None) == 2          # K % 4
+    assert L.lq_gemv(MIS, 8, 64, 2, P, P, 1, P, None, ws, None) == 4        # misaligned w
+    assert L.lq_gemv(P, 8, 64, 2, P, MIS, 1, P, None, ws, None) == 4       # misaligned a_lift
+    assert L.lq_gemv(P, 0, 64, 2, P, P, 1, P, None, ws, None) == 2          # m = 0
+
+
+def test_gemv_workspace_required(L):
+    n = ctypes.c_size_t(0)
+    m, K = 28672, 19456
+    assert L.lq_gemv_workspace_size(m, K, 1, ctypes.byref(n)) == 0
+    assert n.value > 0, "this shape splits K and needs partial sums"
+    assert L.lq_gemv(P, m, K, K // 32, P, P, 1, P, None, 0, None) == 7
+    assert L.lq_gemv(P, m, K, K // 32, P, P, 1, P, P, n.value - 1, None) == 7
+    assert L.lq_gemv_workspace_size(m, K, 0, ctypes.byref(n)) == 2
+    assert L.lq_gemv_workspace_size(m, K, 1, None) == 1
+
+
+def test_lift_validation(L):
+    F16, BF16 = lq.LQ_F16, lq.LQ_BF16
+    ok = dict(B=1, n=1280, tb=128, d=10, D=24)
+
+    def call(a=P, adt=F16, B=1, n=1280, t=P, tdt=F16, tb=128, M=P, d=10, D=24, out=P, odt=0):
+        return L.lq_lift_activations(a, adt, B, n, t, tdt, tb, M, d, D, out, odt, None)
+
+    assert call(a=None) == 1
+    assert call(adt=7) == 3
+    assert call(tb=64) == 5
+    assert call(n=1300) == 2          # not a multiple of 128
+    assert call(n=1280, d=12) == 2    # not a multiple of d
+    assert call(d=0) == 2
+    assert call(D=300) == 2
+    assert call(n=1280, d=64, D=200) == 2   # d*D > 8192
+    assert call(B=0) == 2
+    assert call(t=MIS) == 4
+    assert ok  # the happy path needs a GPU and is covered by the GPU tests
+
+
+def test_gemm_and_pack_validation(L):
+    assert L.lq_gemm(P, 8, 64, 2, P, P, lq.LQ_F32, 512, P, None) == 3       # f32 activations
+    assert L.lq_gemm(P, 8, 60, 2, P, P, lq.LQ_F16, 512, P, None) == 2       # K % 8
+    assert L.lq_gemm(P, 8, 64, 2, P, MIS, lq.LQ_F16, 512, P, None) == 4
+    assert L.lq_gemm(P, 8, 64, 2, P, P, lq.LQ_BF16, 0, P, None) == 2
+    assert L.lq_pack_signs(P, 4, 64, 64, P, 1, None) == 2                   # ldw too small
+    assert L.lq_pack_signs(P, 4, 64, 32, P, 2, None) == 2                   # lds < K
+    assert L.lq_pack_signs(None, 4, 64, 64, P, 2, None) == 1
+    assert L.lq_pack_signs(P, 0, 64, 64, P, 2, None) == 0                   # empty: no-op
+    assert L.lq_unpack_signs(P, 4, 64, 2, None, 64, None) == 1
+    assert L.lq_unpack_signs(P, 4, 0, 0, P, 0, None) == 0                   # empty: no-op
+    assert L.lq_workspace_clear(None, 16, None) == 1
+    assert L.lq_workspace_clear(MIS, 16, None) == 4
+    assert L.lq_workspace_clear(None, 0, None) == 0
+
+
+def test_error_message_is_thread_local_and_cleared(L):
+    import threading
+    assert L.lq_gemv(None, 8, 64, 2, P, P, 1, P, None, 0, None) == 1
+    seen = {}
+
+    def other():
+        seen["msg"] = L.lq_last_error().decode()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["msg"] == ""
+    assert _err(L) != ""
+    assert L.lq_pack_signs(P, 0, 64, 64, P, 2, None) == 0
+    assert _err(L) == ""

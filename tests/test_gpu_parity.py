@@ -1,0 +1,240 @@
+"""GPU parity: the HIP path through the C ABI against the float64 oracle.
+
+Bars (written here, derived in the design notes):
+  * sign pack / unpack: bit-exact.
+  * layer output: e = max_b max_i |o - o_ref| / max_i |o_ref| <= 2e-3, the
+    tolerance stated for 16-bit inputs.  The float32 GEMV path also has to
+    stay under 1e-4 (float32 sums of at most ~7e4 terms of random sign
+    typically lose ~sqrt(K) * 2^-24 ~ 2e-5 relative; 1e-4 leaves margin and
+    still fails any dropped term or wrong sign).
+  * lifted activations: float32 output within 1e-5 (relative to the token's
+    largest value); 16-bit outputs within one unit of rounding of the float32
+    value plus that.
+"""
+import numpy as np
+import pytest
+import torch
+
+from bit_lifted_gemv_amd import lq, synth
+from oracle import lq_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+TOL_F32 = 1e-4
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    lq.load_library()
+    return torch.device("cuda:0")
+
+
+def _up(x, dtype, dev):
+    return lq.to_torch_16(x, dtype).to(dev)
+
+
+def _banner(msg):
+    print(msg, flush=True)
+
+
+# ----------------------------------------------------------------- sign packing
+@pytest.mark.parametrize("rows,K,extra", [(1, 1, 0), (3, 31, 1), (5, 33, 0), (7, 100, 2),
+                                          (64, 3072, 0), (4, 68096, 0), (9, 513, 3)])
+def test_pack_unpack_bit_exact(dev, rows, K, extra):
+    _banner(f"pack rows={rows} K={K}")
+    rng = np.random.default_rng(K * 31 + rows)
+    sg = synth.random_signs_i8(rng, rows, K)
+    sg[rng.random(sg.shape) < 0.05] = 0                      # zeros pack as 0 bits
+    ldw = (K + 31) // 32 + extra
+    want = O.pack_signs_ref(sg, ldw)
+    got = lq.pack_signs(torch.from_numpy(sg).to(dev), ldw=ldw).cpu().numpy().view(np.uint32)
+    np.testing.assert_array_equal(got, want)
+    back = lq.unpack_signs(torch.from_numpy(want.view(np.int32)).to(dev), K).cpu().numpy()
+    np.testing.assert_array_equal(back, O.signs_from_packed(want, K))
+
+
+def test_pack_empty_is_noop(dev):
+    L = lq.lib()
+    assert L.lq_pack_signs(None, 0, 0, 0, None, 0, None) == 0
+    assert L.lq_unpack_signs(None, 0, 5, 1, None, 5, None) == 0
+
+
+# ----------------------------------------------------------------- lift
+LIFT_CASES = [  # (n, d, D, B, act dtype)
+    (1280, 10, 24, 1, "f16"), (640, 10, 24, 3, "bf16"), (1024, 8, 19, 1, "bf16"),
+    (512, 8, 20, 16, "bf16"), (256, 16, 40, 33, "bf16"), (384, 8, 16, 4, "f16"),
+    (384, 3, 7, 2, "bf16"), (256, 64, 128, 1, "f16"),
+]
+
+
+@pytest.mark.parametrize("n,d,D,B,dt", LIFT_CASES)
+def test_lift_float32(dev, n, d, D, B, dt):
+    _banner(f"lift n={n} d={d} D={D} B={B} {dt}")
+    L = synth.make_layer(8, n, d, D, B, seed=n + d + D + B, dtype=dt)
+    ref = O.lift(O.transform(O.decode(L.a, dt), O.decode(L.t_inv, dt)), L.M, d, D)
+    got = lq.lift(_up(L.a, dt, dev), _up(L.t_inv, dt, dev), torch.from_numpy(L.M).to(dev), d, D,
+                  out_dtype=torch.float32).cpu().numpy()
+    err = np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)
+    assert err.max() <= 1e-5, err
+
+
+@pytest.mark.parametrize("odt", [torch.float16, torch.bfloat16])
+def test_lift_16bit_outputs(dev, odt):
+    n, d, D, B = 1024, 8, 19, 5
+    L = synth.make_layer(4, n, d, D, B, seed=3, dtype="bf16")
+    ref = O.lift(O.transform(O.decode(L.a, "bf16"), O.decode(L.t_inv, "bf16")), L.M, d, D)
+    got = lq.lift(_up(L.a, "bf16", dev), _up(L.t_inv, "bf16", dev),
+                  torch.from_numpy(L.M).to(dev), d, D, out_dtype=odt).float().cpu().numpy()
+    u = 2.0 ** -11 if odt == torch.float16 else 2.0 ** -8     # unit roundoff of the output
+    bound = u * np.abs(ref) + 1e-5 * np.abs(ref).max(axis=1, keepdims=True)
+    assert (np.abs(got - ref) <= bound).all()
+
+
+# ----------------------------------------------------------------- GEMV (lifted product)
+GEMV_CASES = [  # (m, K, B): ragged rows, slices and token groups
+    (1, 4, 1), (63, 512, 1), (65, 516, 1), (200, 1544, 2), (129, 3072, 3), (300, 2048, 4),
+    (77, 1000, 5), (1000, 4100, 16), (4096, 10240, 1), (520, 9216, 7),
+]
+
+
+@pytest.mark.parametrize("m,K,B", GEMV_CASES)
+def test_gemv_lifted_product(dev, m, K, B):
+    _banner(f"gemv m={m} K={K} B={B}")
+    rng = np.random.default_rng(m * 7 + K + B)
+    ldw = ((K + 31) // 32 + 1) // 2 * 2
+    packed = synth.random_sign_words(rng, m, K, ldw=ldw)
+    al = rng.standard_normal((B, K)).astype(np.float32)
+    s = rng.uniform(0.01, 0.03, m).astype(np.float32)
+    ref = O.lifted_product(packed, K, al, s)
+    got = lq.gemv(torch.from_numpy(packed.view(np.int32)).to(dev), torch.from_numpy(s).to(dev),
+                  torch.from_numpy(al).to(dev), K).cpu().numpy()
+    e = O.rel_err_colmax(got, ref)
+    assert e <= TOL_F32, e
+
+
+def test_gemv_deterministic(dev):
+    rng = np.random.default_rng(1)
+    m, K = 3000, 19456
+    packed = synth.random_sign_words(rng, m, K)
+    al = torch.from_numpy(rng.standard_normal((1, K)).astype(np.float32)).to(dev)
+    w = torch.from_numpy(packed.view(np.int32)).to(dev)
+    s = torch.ones(m, device=dev)
+    o1 = lq.gemv(w, s, al, K)
+    o2 = lq.gemv(w, s, al, K)
+    assert torch.equal(o1, o2)
+
+
+def test_gemv_all_ones_closed_form(dev):
+    """All signs +1 (and all -1): out = +-s * sum_k a_lift[k]."""
+    m, K = 130, 2560
+    al = np.random.default_rng(2).standard_normal((2, K)).astype(np.float32)
+    s = np.linspace(0.5, 1.5, m).astype(np.float32)
+    for fill, sign in ((0xFFFFFFFF, 1.0), (0, -1.0)):
+        packed = np.full((m, K // 32), fill, dtype=np.uint32)
+        got = lq.gemv(torch.from_numpy(packed.view(np.int32)).to(dev),
+                      torch.from_numpy(s).to(dev), torch.from_numpy(al).to(dev), K).cpu().numpy()
+        want = sign * s[None, :] * al.astype(np.float64).sum(axis=1)[:, None]
+        assert O.rel_err_colmax(got, want) <= TOL_F32
+
+
+# ----------------------------------------------------------------- GEMM
+GEMM_CASES = [  # (m, K, B)
+    (128, 256, 128), (200, 520, 130), (33, 64, 1), (1000, 2048, 300), (256, 20480, 64),
+]
+
+
+@pytest.mark.parametrize("odt", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("m,K,B", GEMM_CASES)
+def test_gemm_lifted_product(dev, m, K, B, odt):
+    _banner(f"gemm m={m} K={K} B={B} {odt}")
+    rng = np.random.default_rng(m + K + B)
+    ldw = (K + 31) // 32
+    packed = synth.random_sign_words(rng, m, K, ldw=ldw)
+    al = torch.from_numpy(rng.standard_normal((B, K)).astype(np.float32)).to(odt)
+    s = rng.uniform(0.01, 0.03, m).astype(np.float32)
+    # the oracle sees exactly the stored 16-bit activations
+    ref = O.lifted_product(packed, K, al.float().numpy(), s)
+    got = lq.gemm(torch.from_numpy(packed.view(np.int32)).to(dev), torch.from_numpy(s).to(dev),
+                  al.to(dev), K).cpu().numpy()
+    e = O.rel_err_colmax(got, ref)
+    assert e <= 1e-4, e   # operands are exact; float32 accumulation only
+
+
+def test_gemm_one_hot_unpacks_signs_exactly(dev):
+    """D = d, M = I, T^-1 = I, s = 1, tokens = identity columns: the GEMM
+    output is the +-1 sign matrix itself, bit for bit."""
+    m, n = 200, 256
+    L = synth.make_layer(m, n, 4, 4, 1, seed=5, identity_t=True)
+    eye = np.eye(n, dtype=np.float32)
+    dl = lq.DeviceLayer(L.packed, np.eye(4, dtype=np.float32), L.t_inv, np.ones(m, np.float32),
+                        4, 4, n, "bf16", device=dev)
+    for gdt in (torch.float16, torch.bfloat16):
+        out = dl.forward(torch.from_numpy(eye).to(dev).to(torch.bfloat16), gemm_dtype=gdt,
+                         path="gemm").cpu().numpy()
+        np.testing.assert_array_equal(out, O.signs_from_packed(L.packed, n).T.astype(np.float32))
+
+
+# ----------------------------------------------------------------- whole layer
+def test_integer_special_case_exact(dev):
+    """D = d, M = I, T^-1 = I, s = 1, small-integer activations: exact integers."""
+    m, n, B = 300, 1024, 3
+    L = synth.make_layer(m, n, 8, 8, B, seed=6, identity_t=True)
+    a_int = np.random.default_rng(4).integers(-20, 21, (B, n)).astype(np.float32)
+    a = synth.to_storage(a_int, "bf16")
+    dl = lq.DeviceLayer(L.packed, np.eye(8, dtype=np.float32), L.t_inv, np.ones(m, np.float32),
+                        8, 8, n, "bf16", device=dev)
+    want = O.forward(L.packed, n, np.eye(8, dtype=np.float32), L.t_inv, np.ones(m, np.float32), a,
+                     8, 8, "bf16")
+    for path in ("gemv", "gemm"):
+        got = dl.forward(_up(a, "bf16", dev), path=path).cpu().numpy()
+        np.testing.assert_array_equal(got, want)
+
+
+LAYER_CASES = [  # (m, n, d, D, B, dtype): small layers the oracle does in full
+    (130, 1280, 10, 24, 1, "f16"), (257, 1024, 8, 20, 1, "bf16"), (96, 2048, 8, 16, 4, "bf16"),
+    (500, 1024, 8, 19, 16, "bf16"), (256, 512, 16, 40, 130, "bf16"),
+]
+
+
+@pytest.mark.parametrize("m,n,d,D,B,dt", LAYER_CASES)
+def test_layer_small(dev, m, n, d, D, B, dt):
+    _banner(f"layer m={m} n={n} D/d={D}/{d} B={B}")
+    L = synth.make_layer(m, n, d, D, B, seed=m + n + B, dtype=dt, outlier_frac=0.01)
+    ref = O.forward(L.packed, L.K, L.M, L.t_inv, L.s, L.a, d, D, dt)
+    dl = lq.DeviceLayer.from_synth(L, device=dev)
+    got = dl.forward(_up(L.a, dt, dev)).cpu().numpy()
+    e = O.rel_err_colmax(got, ref)
+    assert e <= TOL, e
+    if B <= 16:
+        assert e <= TOL_F32, e
+
+
+def _sample_rows(m, rng, k=96):
+    head = np.arange(min(64, m))
+    tail = np.arange(max(0, m - 64), m)
+    mid = rng.choice(m, size=min(k, m), replace=False)
+    return np.unique(np.concatenate([head, tail, mid]))
+
+
+CASES = synth.all_cases()
+
+
+@pytest.mark.parametrize("cfg,si,shape,B", CASES,
+                         ids=[f"cfg{c.index}-{s[0]}x{s[1]}-B{b}" for c, _, s, b in CASES])
+def test_full_size_case(dev, cfg, si, shape, B):
+    """Every workload case at its full size, in the configuration the
+    benchmark runs, checked on sampled rows (first and last 64 rows plus 96
+    random ones) against the oracle."""
+    m, n = shape
+    _banner(f"full {cfg.name} {m}x{n} B={B}")
+    L = synth.make_case(cfg, si, B)
+    dl = lq.DeviceLayer.from_synth(L, device=dev)
+    got = dl.forward(_up(L.a, L.dtype, dev)).cpu().numpy()
+    rows = _sample_rows(m, np.random.default_rng(si + B))
+    ref = O.forward(L.packed, L.K, L.M, L.t_inv, L.s, L.a, L.d, L.D, L.dtype, rows=rows)
+    e = O.rel_err_colmax(got[:, rows], ref)
+    _banner(f"  rel err {e:.3e}")
+    assert e <= TOL, e
+    assert np.isfinite(got).all()
