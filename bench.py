@@ -1,0 +1,336 @@
+"""Benchmark of the LiftQuant layer on one MI355X.
+
+A step is one pass of the layer's hot path over one batch: for the 70B-class
+LQ-19/8 MLP pair at batch 1 (up 28672 x 8192, then down 8192 x 28672) each
+projection runs the activation lift (T^-1 blocks, then M^T per group) and the
+packed-sign GEMV with its diag(s) epilogue.  Inputs are resident in HBM and
+rotate over enough copies (> 2x the 256 MB Infinity Cache) that every step
+reads its weights from HBM.
+
+Printed: one JSON line with the whole-step algorithmic GB/s (`value`), the
+dominant kernel's roofline (GEMV: algorithmic bytes per launch / its average
+duration from HIP events on its stream), the batch-512 MFMA GEMM in TFLOP/s,
+per-workload GEMV figures, and the float64 oracle timed on the host cores over
+a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}   # dense
+MALL_BYTES = 256 << 20
+METRIC = ("LQ GEMV achieved HBM GB/s (% of peak) at batch 1; "
+          "MFMA TFLOP/s at batch 512")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--gemm-dtype", default="f16", choices=["f16", "bf16"])
+    p.add_argument("--no-cases", action="store_true", help="skip the per-workload sweep")
+    p.add_argument("--only", default="all", choices=["all", "layer", "gemm"],
+                   help="layer: only the timed 70B steps; gemm: only the batch-512 GEMM")
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------- byte counts
+def gemv_bytes(m, K, B):
+    """Algorithmic bytes of one GEMV launch: weights, scales, lifted activations, output."""
+    return m * K // 8 + 4 * m + 4 * K * B + 4 * m * B
+
+
+def lift_bytes(n, d, D, B, act_bytes=2, out_bytes=4):
+    K = n // d * D
+    return act_bytes * n * B + 2 * n * 128 + 4 * d * D + out_bytes * K * B
+
+
+def layer_bytes(m, n, d, D, B):
+    """Whole layer: a, T^-1 (16-bit), M, W_q, s, o; the a_hat round trip excluded."""
+    K = n // d * D
+    return 2 * n * B + 2 * n * 128 + 4 * d * D + m * K // 8 + 4 * m + 4 * m * B
+
+
+def src_sha(name):
+    path = os.path.join(ROOT, "bit_lifted_gemv_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_src, key):
+    """HBM bytes per launch from a committed counter summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+        ent = data.get(key)
+        if ent and ent.get("source_sha") == src_sha(kernel_src):
+            return ent.get("hbm_bytes_per_launch")
+    except (ValueError, OSError):
+        return None
+    return None
+
+
+# ----------------------------------------------------------------- GPU side
+class Rotation:
+    """R device copies of a layer so that R * footprint > 2 x MALL."""
+
+    def __init__(self, L, torch, lq, dev, min_bytes=2 * MALL_BYTES):
+        base = lq.DeviceLayer.from_synth(L, device=dev)
+        foot = base.w.numel() * 4 + base.t_inv.numel() * 2 + base.s.numel() * 4
+        self.R = max(2, int(np.ceil(min_bytes / foot)))
+        self.copies = [base]
+        for _ in range(self.R - 1):
+            c = lq.DeviceLayer.__new__(lq.DeviceLayer)
+            c.__dict__.update(base.__dict__)
+            c.w = base.w.clone()
+            c.t_inv = base.t_inv.clone()
+            c.s = base.s.clone()
+            c.M = base.M.clone()
+            self.copies.append(c)
+        self.a = lq.to_torch_16(L.a, L.dtype).to(dev)
+        self.L = L
+
+    def __getitem__(self, i):
+        return self.copies[i % self.R]
+
+
+def run_gpu(args):
+    import torch
+
+    from bit_lifted_gemv_amd import lq, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lq.load_library()
+    if args.only == "gemm":
+        return dict(gemm=run_gemm(args, torch, lq, synth, dev))
+    cfg = synth.CONFIGS[3]                     # LQ-19/8 70B-class MLP
+    layers = [synth.make_case(cfg, si, 1) for si in range(len(cfg.shapes))]
+    rots = [Rotation(L, torch, lq, dev) for L in layers]
+    st = torch.cuda.current_stream()
+    # lifted activations and outputs, allocated once
+    al = [torch.empty((1, L.K), dtype=torch.float32, device=dev) for L in layers]
+    outs = [torch.empty((1, L.m), dtype=torch.float32, device=dev) for L in layers]
+
+    ev = {}
+
+    def step(i, record=False):
+        for j, (rot, L) in enumerate(zip(rots, layers)):
+            c = rot[i]
+            lq.lift(rot.a, c.t_inv, c.M, L.d, L.D, out=al[j])
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(st)
+            lq.gemv(c.w, c.s, al[j], L.K, out=outs[j])
+            if record:
+                e1.record(st)
+                ev.setdefault(j, []).append((e0, e1))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, record=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    step_bytes = sum(layer_bytes(L.m, L.n, L.d, L.D, 1) for L in layers)
+    value = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # dominant kernel: GEMV; per-launch durations from the event pairs
+    per = {}
+    for j, L in enumerate(layers):
+        d_ms = [a.elapsed_time(b) for a, b in ev[j]]
+        per[j] = float(np.mean(d_ms))
+    g_bytes = [gemv_bytes(L.m, L.K, 1) for L in layers]
+    gemv_ms = sum(per.values()) / len(per)
+    gemv_bytes_avg = sum(g_bytes) / len(g_bytes)
+    achieved = gemv_bytes_avg / (gemv_ms * 1e-3) / 1e9
+    traffic = load_traffic("k_gemv.hip", "gemv_lq19_8_70b_b1")
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "gemv_lut_kernel", "bytes_per_launch": int(gemv_bytes_avg),
+                "avg_launch_us": round(gemv_ms * 1e3, 3),
+                "per_shape_us": {f"{L.m}x{L.n}": round(per[j] * 1e3, 3)
+                                 for j, L in enumerate(layers)}}
+    outs_host = [o.cpu().numpy().copy() for o in outs]
+    rot_info = {"copies": rots[0].R, "bytes_per_copy": int(layers[0].packed.nbytes)}
+
+    gemm = None if args.only == "layer" else run_gemm(args, torch, lq, synth, dev)
+    cases = None if (args.no_cases or args.only != "all") else run_cases(torch, lq, synth, dev)
+    return dict(value=value, ms_step=ms_step, roofline=roofline, gemm=gemm, cases=cases,
+                layers=layers, outs=outs_host, rot=rot_info, step_bytes=step_bytes)
+
+
+def time_launches(torch, fn, n, st):
+    """Average duration of fn() over n back-to-back calls, HIP events on st."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for i in range(n):
+        fn(i)
+    e1.record(st)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def run_gemm(args, torch, lq, synth, dev):
+    """Batch-512 LQ-40/16 GEMM: lift to 16-bit, then the MFMA contraction."""
+    cfg = synth.CONFIGS[4]
+    L = synth.make_case(cfg, 0, cfg.batches[0])
+    rot = Rotation(L, torch, lq, dev)
+    odt = torch.float16 if args.gemm_dtype == "f16" else torch.bfloat16
+    als = [torch.empty((L.B, L.K), dtype=odt, device=dev) for _ in range(2)]
+    out = torch.empty((L.B, L.m), dtype=torch.float32, device=dev)
+    st = torch.cuda.current_stream()
+    for i in range(3):
+        c = rot[i]
+        lq.lift(rot.a, c.t_inv, c.M, L.d, L.D, out=als[i % 2])
+        lq.gemm(c.w, c.s, als[i % 2], L.K, out=out)
+    torch.cuda.synchronize()
+    n = max(5, min(args.steps, 40))
+    lift_ms = time_launches(torch, lambda i: lq.lift(rot.a, rot[i].t_inv, rot[i].M, L.d, L.D,
+                                                     out=als[i % 2]), n, st)
+    gemm_ms = time_launches(torch, lambda i: lq.gemm(rot[i].w, rot[i].s, als[i % 2], L.K, out=out),
+                            n, st)
+    flops = 2.0 * L.m * L.K * L.B
+    tf = flops / (gemm_ms * 1e-3) / 1e12
+    return {"workload": f"LQ-40/16 {L.m}x{L.n} batch {L.B}, lifted K={L.K}",
+            "operand_dtype": args.gemm_dtype, "gemm_us": round(gemm_ms * 1e3, 2),
+            "lift_us": round(lift_ms * 1e3, 2), "tflops": round(tf, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 1),
+                         "peak": MFMA_PEAK_TFLOPS[args.gemm_dtype], "unit": "TFLOP/s",
+                         "frac": round(tf / MFMA_PEAK_TFLOPS[args.gemm_dtype], 4),
+                         "traffic": load_traffic("k_gemm.hip", "gemm_lq40_16_b512"),
+                         "flops_per_launch": flops}}
+
+
+def run_cases(torch, lq, synth, dev):
+    """GEMV (B <= 16) per workload case: back-to-back launches on rotating copies."""
+    res = []
+    st = torch.cuda.current_stream()
+    for cfg, si, (m, n), B in synth.all_cases():
+        if B > 16:
+            continue
+        L = synth.make_case(cfg, si, B)
+        rot = Rotation(L, torch, lq, dev)
+        al = torch.empty((B, L.K), dtype=torch.float32, device=dev)
+        out = torch.empty((B, m), dtype=torch.float32, device=dev)
+        lq.lift(rot.a, rot[0].t_inv, rot[0].M, L.d, L.D, out=al)
+        for i in range(3):
+            lq.gemv(rot[i].w, rot[i].s, al, L.K, out=out)
+        torch.cuda.synchronize()
+        g = time_launches(torch, lambda i: lq.gemv(rot[i].w, rot[i].s, al, L.K, out=out), 30, st)
+        lt = time_launches(torch, lambda i: lq.lift(rot.a, rot[i].t_inv, rot[i].M, L.d, L.D,
+                                                    out=al), 30, st)
+        gb = gemv_bytes(m, L.K, B) / (g * 1e-3) / 1e9
+        res.append({"case": f"{cfg.name} {m}x{n} B={B}", "gemv_us": round(g * 1e3, 2),
+                    "gemv_GBs": round(gb, 1), "gemv_frac": round(gb / HBM_PEAK_GBS, 3),
+                    "lift_us": round(lt * 1e3, 2)})
+        del rot
+        torch.cuda.empty_cache()
+    return res
+
+
+# ----------------------------------------------------------------- CPU baseline
+def cpu_baseline(layers, outs, seconds):
+    """The float64 oracle (as it stands) on a bounded sample of the same
+    workload: whole rows of the up and down projections, chunk by chunk, until
+    about `seconds` of work; reported in the same unit as `value`."""
+    from oracle import lq_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:   # noqa: BLE001
+        threads = os.cpu_count()
+    total_t = 0.0
+    total_bytes = 0
+    rows_done = [0, 0]
+    max_err = 0.0
+    chunk = 1024
+    # the lift part (T^-1 and M for the whole layer) is paid once per layer
+    j = 0
+    while total_t < seconds and any(r < L.m for r, L in zip(rows_done, layers)):
+        L = layers[j % len(layers)]
+        r0 = rows_done[j % len(layers)]
+        if r0 >= L.m:
+            j += 1
+            continue
+        rows = np.arange(r0, min(r0 + chunk, L.m))
+        t0 = time.perf_counter()
+        ref = O.forward(L.packed, L.K, L.M, L.t_inv, L.s, L.a, L.d, L.D, L.dtype, rows=rows)
+        dt = time.perf_counter() - t0
+        total_t += dt
+        total_bytes += rows.size * (L.K // 8 + 4 + 4 * L.B)
+        if r0 == 0:
+            total_bytes += 2 * L.n * L.B + 2 * L.n * 128 + 4 * L.d * L.D
+        got = outs[j % len(layers)][:, rows]
+        max_err = max(max_err, O.rel_err_colmax(got, ref))
+        rows_done[j % len(layers)] = rows[-1] + 1
+        j += 1
+    gbs = total_bytes / total_t / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 oracle (unpack, W_hat = M y, T^-1 a, dgemm) on rows "
+                      f"{rows_done[0]} of 28672 (up) and {rows_done[1]} of 8192 (down), "
+                      f"{total_t:.1f} s of CPU time",
+            "seconds": round(total_t, 2), "gpu_vs_oracle_max_rel_err": float(f"{max_err:.3e}")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              f"(this path is single-GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    r = run_gpu(args)
+    if args.only == "gemm":
+        print(json.dumps({"gemm": r["gemm"]}), flush=True)
+        return
+    cpu = None if args.no_cpu else cpu_baseline(r["layers"], r["outs"], args.cpu_seconds)
+    line = {
+        "metric": METRIC,
+        "value": round(r["value"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; shapes of the 70B-class LQ-19/8 MLP)",
+        "config": {"workload": "LQ-19/8 70B-class MLP at batch 1: up 28672x8192 then down "
+                               "8192x28672, lift + GEMV each, inputs bf16, weights 2.375 bit",
+                   "batch": 1, "step_bytes": r["step_bytes"], "rotation": r["rot"]},
+        "frac_of_hbm_peak": round(r["value"] / HBM_PEAK_GBS, 4),
+        "roofline": r["roofline"],
+        "cpu_baseline": cpu,
+        "gemm": r["gemm"],
+        "cases": r["cases"],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -3,40 +3,42 @@
 // (LiftQuant notes, 关键设计 4: after the activation transform the layer is a
 // product of 1-bit weights with floats, scaled per row by s).
 //
-// The weights stream from HBM once; the kernel is bound by HBM bandwidth as
-// long as the work per weight bit stays small.  One vector op per bit would
-// already be too slow on gfx950 (64 lanes x 4 SIMDs x 2.4 GHz = 39 T lane-ops/s
-// against 64 T weight bits/s at 8 TB/s), so the sign-select is done a byte at a
-// time through a table of activation sums:
+// The weights stream from HBM once, so the kernel is bound by HBM bandwidth
+// as long as the work per weight bit stays small.  One vector op per bit
+// would already be too slow on gfx950 (64 lanes x 4 SIMDs x 2.4 GHz = 39 T
+// lane-ops/s against 64 T weight bits/s at 8 TB/s), so the sign-select is done
+// a byte at a time through tables of activation sums:
 //   E_p[v] = sum_{t<8} (2*bit_t(v) - 1) * a_hat[8p + t]     (v = 0..255)
-// for the 64 byte positions p of a 512-bit slice of the lifted dimension.
-// The sum over a weight row is then one table read and one add per byte.
-// The tables hold activation sums, rebuilt from a_hat on every call; nothing
-// about the weights is tabulated.
+// for the 128 byte positions p of a 1024-bit slice of the lifted dimension.
+// A row's sum is then one table read and one add per weight byte.  The tables
+// hold activation sums rebuilt from a_hat on every call; nothing about the
+// weights is tabulated.
 //
-// LDS layout: entry (slot, v) at byte 256*v + 4*slot, 64 slots x 256 entries
-// = 64 KB per workgroup (two workgroups per CU).  A byte of weights turns into
-// its table address with a single v_perm_b32 (weight byte -> address byte 1,
-// lane constant 4*slot -> address byte 0).  Lanes are laid out so that the 32
-// lanes of each half-wave read 32 different slots whose banks (slot mod 32)
-// are all distinct: reads are free of bank conflicts.
+// LDS layout (128 KB, one workgroup per CU): entry (slot, v) at byte
+// 65536*(slot >> 6) + 256*v + 4*(slot & 63).  A weight byte becomes its
+// table address with one v_perm_b32: the weight byte goes to address byte 1,
+// a per-lane constant supplies bytes 0 and 2.  Lanes are arranged so that the
+// 32 lanes of each half-wave hit 32 different banks on every read.
 //
-// Work split: a workgroup owns 64*JR rows and a run of slices (a K-part).  Per
-// slice it loads its weights (8 bytes per lane per 8-row group), builds the
-// table for each token (8 waves x 32 entries, Gray-code order: one add per
-// entry), and accumulates.  With more than one K-part the partial sums go to
-// a workspace and the last workgroup of a row block (arrival counter) adds
-// them in part order, so the result is deterministic.
+// Work split (persistent, stream-K): the iteration space is ordered
+// (row block, slice, 64-row step) and cut into one equal range per CU, so the
+// load is balanced to one 64-row step.  A workgroup walks its range a unit
+// (row block x slice) at a time: it requests the next unit's weights (8
+// rows x 128 B per wave per step, 16 B per lane) two units ahead, builds the
+// current unit's table, and does the lookups.  A row block owned by one workgroup is written
+// straight to the output; a row block split over several workgroups leaves
+// one partial sum per workgroup in the workspace, and the last of them to
+// arrive (arrival counter) adds them in workgroup order, so the result is
+// deterministic.
 #include "lq_internal.h"
 
 namespace lq {
 namespace {
 
-constexpr int kThreads = 512;              // 8 waves
-constexpr int kWaves = kThreads / 64;
-constexpr int kSliceBits = 512;
-constexpr int kSliceWords = kSliceBits / 32;   // 16
-constexpr int kTableFloats = 64 * 256;         // 64 KB
+constexpr int kSliceBits = 1024;
+constexpr int kSliceBytes = kSliceBits / 8;    // 128
+constexpr int kTableFloats = 128 * 256;        // 128 KB
+constexpr uint32_t kNoLoad = 0x80000000u;      // outside every buffer resource
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_add(float v) {
@@ -53,90 +55,143 @@ __device__ __forceinline__ float sum8(float v) {
 }
 
 __host__ __device__ constexpr int gray(int i) { return i ^ (i >> 1); }
-__host__ __device__ constexpr int ctz5(int i) {
-  return (i & 1) ? 0 : (i & 2) ? 1 : (i & 4) ? 2 : (i & 8) ? 3 : 4;
+__host__ __device__ constexpr int ctz6(int i) {
+  return (i & 1) ? 0 : (i & 2) ? 1 : (i & 4) ? 2 : (i & 8) ? 3 : (i & 16) ? 4 : 5;
 }
 
-// Lifted activations of byte position `lane` of slice `sl` for one token
-// (zero past K; K is a multiple of 4).
-__device__ __forceinline__ void load_x(const float* __restrict__ ah_tok, int64_t K, int sl,
-                                       int lane, float4& x0, float4& x1) {
-  const int64_t k0 = (int64_t)sl * kSliceBits + 8 * lane;
-  x0 = make_float4(0.f, 0.f, 0.f, 0.f);
-  x1 = x0;
-  if (k0 + 4 <= K) x0 = *reinterpret_cast<const float4*>(ah_tok + k0);
-  if (k0 + 8 <= K) x1 = *reinterpret_cast<const float4*>(ah_tok + k0 + 4);
+// Slot of byte position p (and back: the map is an involution).  Byte b of
+// dword d of 16-byte chunk c: p = 16c + 4d + b -> 16c + 4(d ^ (c >> 1)) + b.
+__host__ __device__ constexpr int slot_of(int p) {
+  return (p & ~12) | ((((p >> 2) & 3) ^ ((p >> 5) & 3)) << 2);
 }
 
-// Build the 64 x 256 table of one slice and token: wave w writes entries
-// v in [32w, 32w + 32) of every slot, lane p owns byte position p.
+// Activations of byte position p of slice sl for token t (zero past K).
+__device__ __forceinline__ void load_x(__amdgpu_buffer_rsrc_t ares, int64_t K, int t, int sl,
+                                       int p, float4& x0, float4& x1) {
+  const int64_t k0 = (int64_t)sl * kSliceBits + 8 * p;
+  const uint32_t base = static_cast<uint32_t>(((int64_t)t * K + k0) * 4);
+  const uint32_t o0 = (k0 + 4 <= K) ? base : kNoLoad;
+  const uint32_t o1 = (k0 + 8 <= K) ? base + 16 : kNoLoad;
+  const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(ares, o0, 0, 0);
+  const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(ares, o1, 0, 0);
+  __builtin_memcpy(&x0, &v0, 16);
+  __builtin_memcpy(&x1, &v1, 16);
+}
+
+// Table of one slice and token, built by WAVES waves.  Wave w: slot half
+// h = w & 1 (slots 64h .. 64h + 63, one per lane), entry block q = w >> 1
+// (v in [E*q, E*q + E), E = 512 / WAVES entries), low bits of v visited in
+// Gray-code order: one add per entry.
+template <int WAVES>
 __device__ __forceinline__ void build_table(float* __restrict__ table, const float4& x0,
                                             const float4& x1, int wave, int lane) {
-  const int p = lane;
-  const int slot = p ^ ((p >> 5) << 2);
+  constexpr int E = 512 / WAVES;                 // entries per lane: 64 or 32
+  constexpr int LB = E == 64 ? 6 : 5;            // Gray-coded low bits
+  const int h = wave & 1;
+  const int q = wave >> 1;
   const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-  // v0 = 32*wave: bits 0..4 clear, bits 5..7 = wave bits 0..2
-  float val = -(x[0] + x[1] + x[2] + x[3] + x[4]);
-  val += (wave & 1) ? x[5] : -x[5];
-  val += (wave & 2) ? x[6] : -x[6];
-  val += (wave & 4) ? x[7] : -x[7];
-  float tw[5];
+  float val = 0.f;
 #pragma unroll
-  for (int t = 0; t < 5; ++t) tw[t] = 2.f * x[t];
-  float* base = table + (32 * wave) * 64 + slot;
+  for (int t = 0; t < LB; ++t) val -= x[t];
+#pragma unroll
+  for (int t = LB; t < 8; ++t) val += ((q >> (t - LB)) & 1) ? x[t] : -x[t];
+  float tw[LB];
+#pragma unroll
+  for (int t = 0; t < LB; ++t) tw[t] = 2.f * x[t];
+  float* base = table + h * 16384 + (E * q) * 64 + lane;
   base[0] = val;
 #pragma unroll
-  for (int i = 1; i < 32; ++i) {
-    const int t = ctz5(i);
+  for (int i = 1; i < E; ++i) {
+    const int t = ctz6(i);
     const bool up = (gray(i) >> t) & 1;
     val = up ? val + tw[t] : val - tw[t];
     base[gray(i) * 64] = val;
   }
 }
 
-template <int NT, int JR>
-__global__ void __launch_bounds__(kThreads, 2) gemv_lut_kernel(
+struct Sched {
+  int64_t T;        // 64-row steps in the iteration space (row blocks x slices x JR)
+  int G;            // workgroups
+  int S;            // slices
+  int rbs;          // row blocks
+  int kmax;         // most workgroups sharing one row block
+};
+
+// Workgroup whose range holds step g: the largest w with floor(w*T/G) <= g.
+__host__ __device__ __forceinline__ int owner(int64_t g, int64_t T, int G) {
+  return static_cast<int>(((g + 1) * G + T - 1) / T - 1);
+}
+
+// THREADS: workgroup size (8 or 16 waves); NT: tokens per launch (tables are
+// rebuilt per token, weights stay in registers); JR: row steps per unit (a
+// row step is 8 rows per wave); DEPTH: units of weights held in registers
+// (DEPTH - 1 of them in flight behind the current one).
+template <int THREADS, int NT, int JR, int DEPTH>
+__global__ void __launch_bounds__(THREADS, 1) gemv_lut_kernel(
     const uint32_t* __restrict__ w, int64_t m, int64_t K, int64_t ldw, const float* __restrict__ s,
     const float* __restrict__ ah, int B, float* __restrict__ out, float* __restrict__ partials,
-    unsigned* __restrict__ counters, int slices_per_part, int parts, int slices,
-    uint32_t w_bytes) {
+    unsigned* __restrict__ counters, Sched sc, uint32_t w_bytes, uint32_t a_bytes) {
   __shared__ float table[kTableFloats];
+  __shared__ float4 xstage[2][256];   // activations of a slice, by slot (double-buffered)
   __shared__ int s_last;
 
+  constexpr int kThreads = THREADS;
+  constexpr int kWaves = THREADS / 64;
+  constexpr int kRowsPerStep = kWaves * 8;
+  constexpr int R = kRowsPerStep * JR;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int rb = blockIdx.x / parts;
-  const int part = blockIdx.x - rb * parts;
-  constexpr int R = 64 * JR;
-  const int64_t row0 = (int64_t)rb * R;
-  const int sl0 = part * slices_per_part;
-  const int sl1 = min(sl0 + slices_per_part, slices);
+  const int wg = blockIdx.x;
+  const int64_t g_begin = (int64_t)wg * sc.T / sc.G;
+  const int64_t g_end = (int64_t)(wg + 1) * sc.T / sc.G;
+  if (g_begin >= g_end) return;
+  const int64_t u_begin = g_begin / JR;
+  const int64_t u_last = (g_end - 1) / JR;
 
-  // lane -> (row within an 8-row group, 8-byte chunk of the 64-byte slice row)
-  const int rsub = lane >> 3;
+  // lane -> (row r of the wave's 8 rows, 16-byte chunk c of the 128-byte slice row)
+  const int r = lane >> 3;
   const int c = lane & 7;
-  const int r4 = rsub & 3;
-  // address bytes 4*slot for byte b of dword dd: slot = 8c + 4(dd ^ [c>=4]) + b
-  uint32_t lc[2];
-#pragma unroll
-  for (int dd = 0; dd < 2; ++dd) {
-    uint32_t v = 0;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t a4 = 4u * (8u * c + 4u * (dd ^ (c >= 4 ? 1 : 0)) + b);
-      v |= a4 << (8 * b);
-    }
-    lc[dd] = v;
-  }
-  // selector of step i: byte b = (i + r4) & 3 of the weight dword goes to the
-  // address byte 1, byte b of the lane constant to byte 0, zeros above.
+  const int r4 = r & 3;
+  uint32_t lc[4][4];
   uint32_t sel[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t b = (i + r4) & 3;
-    sel[i] = b | ((4u + b) << 8) | 0x0C0C0000u;
+    sel[i] = 0u | ((4u + b) << 8) | (2u << 16) | (0x0Cu << 24);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int sl = slot_of(16 * c + 4 * d + static_cast<int>(b));
+      lc[d][i] = static_cast<uint32_t>(4 * (sl & 63)) | (static_cast<uint32_t>(sl >> 6) << 16);
+    }
   }
+  // byte position whose table entries this lane writes (slot 64h + lane)
+  const int my_pos = slot_of(64 * (wave & 1) + lane);
+
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(w), (short)0, static_cast<int>(w_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(ah), (short)0, static_cast<int>(a_bytes), 0x00020000);
+  const uint32_t row_bytes = static_cast<uint32_t>(ldw * 4);
+
+  // Weights of unit u, 64-row steps [j_lo, j_hi) only (the rest load nothing).
+  auto load_unit = [&](int64_t u, uint4* wv) {
+    const bool ok = u <= u_last;
+    const int64_t rb = u / sc.S;
+    const int sl = static_cast<int>(u - rb * sc.S);
+    const int j_lo = (ok && u == u_begin) ? static_cast<int>(g_begin - u * JR) : 0;
+    const int j_hi = (ok && u == u_last) ? static_cast<int>(g_end - u * JR) : JR;
+    const uint32_t base = static_cast<uint32_t>(
+        (rb * R + wave * 8 + r) * (int64_t)row_bytes + (int64_t)sl * kSliceBytes + 16 * c);
+#pragma unroll
+    for (int j = 0; j < JR; ++j) {
+      const uint32_t off = (ok && j >= j_lo && j < j_hi)
+                               ? base + static_cast<uint32_t>(j * kRowsPerStep) * row_bytes
+                               : kNoLoad;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, 0);
+      __builtin_memcpy(&wv[j], &v, 16);
+    }
+  };
 
   float acc[NT][JR];
 #pragma unroll
@@ -144,168 +199,462 @@ __global__ void __launch_bounds__(kThreads, 2) gemv_lut_kernel(
 #pragma unroll
     for (int j = 0; j < JR; ++j) acc[t][j] = 0.f;
 
-  // Software pipeline over steps (slice, token): the activations of the next
-  // step and the weights of the next slice are requested before the current
-  // table is built, so their latency hides behind the build and the lookups.
-  // Weight loads go through a buffer resource sized to the whole weight array:
-  // lanes past the last row read zeros without a branch.  Words past K (and
-  // past ldw, which would belong to the next row) multiply table entries that
-  // are zero, because the activations past K are zero.
-  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t*>(w), (short)0, static_cast<int>(w_bytes), 0x00020000);
-  const uint32_t lane_off = static_cast<uint32_t>(((row0 + wave * 8 + rsub) * ldw + 2 * c) * 4);
-  const uint32_t jstride = static_cast<uint32_t>(kWaves * 8 * ldw * 4);
-  auto load_w = [&](int sl, uint2* wv) {
-    const uint32_t soff = static_cast<uint32_t>(sl) * (kSliceWords * 4);
+  // Flush row block rb (all of its rows this workgroup touched).
+  auto flush = [&](int64_t rb) {
 #pragma unroll
-    for (int j = 0; j < JR; ++j) {
-      const auto v = __builtin_amdgcn_raw_buffer_load_b64(wres, lane_off + j * jstride, soff, 0);
-      __builtin_memcpy(&wv[j], &v, 8);
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < JR; ++j) acc[t][j] = sum8(acc[t][j]);
+    const int64_t g0 = rb * sc.S * JR;
+    const int w_first = owner(g0, sc.T, sc.G);
+    const int w_last = owner(g0 + (int64_t)sc.S * JR - 1, sc.T, sc.G);
+    const int n = w_last - w_first + 1;
+    if (n == 1) {
+      if (c == 0) {
+#pragma unroll
+        for (int j = 0; j < JR; ++j) {
+          const int64_t row = rb * R + j * kRowsPerStep + wave * 8 + r;
+          if (row < m) {
+            const float scale = s[row];
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+              if (t < B) out[(int64_t)t * m + row] = scale * acc[t][j];
+          }
+        }
+      }
+    } else {
+      // partials[rb][k][t][R], k = this workgroup's place among the n sharers;
+      // written and read with device-scope accesses (no cache-wide fences)
+      const int k = wg - w_first;
+      float* pb = partials + ((rb * sc.kmax + k) * (int64_t)NT) * R;
+      if (c == 0) {
+#pragma unroll
+        for (int j = 0; j < JR; ++j) {
+          const int rr = j * kRowsPerStep + wave * 8 + r;
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            __hip_atomic_store(pb + t * R + rr, acc[t][j], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(&counters[rb], 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == static_cast<unsigned>(n - 1)) ? 1 : 0;
+      }
+      __syncthreads();
+      if (s_last) {
+        const float* p0 = partials + (rb * sc.kmax * (int64_t)NT) * R;
+        for (int i = tid; i < NT * R; i += kThreads) {
+          const int t = i / R;
+          const int rr = i - t * R;
+          const int64_t row = rb * R + rr;
+          if (t < B && row < m) {
+            // batches of 8 independent loads, added in part order
+            const float* pp = p0 + (int64_t)t * R + rr;
+            const int64_t stride = (int64_t)NT * R;
+            float sum = 0.f;
+            for (int k0 = 0; k0 < n; k0 += 8) {
+              float v[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                v[e] = (k0 + e < n) ? __hip_atomic_load(pp + (k0 + e) * stride, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT)
+                                    : 0.f;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) sum += v[e];
+            }
+            out[(int64_t)t * m + row] = s[row] * sum;
+          }
+        }
+        if (tid == 0)
+          __hip_atomic_store(&counters[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < JR; ++j) acc[t][j] = 0.f;
   };
-  uint2 wv[JR], wn[JR];
-  float4 xc0, xc1, xn0, xn1;
-  if (sl0 < sl1) {
-    load_x(ah, K, sl0, lane, xc0, xc1);
-    load_w(sl0, wv);
-  }
+
   const char* tb = reinterpret_cast<const char*>(table);
-  for (int sl = sl0; sl < sl1; ++sl) {
+  uint4 wbuf[DEPTH][JR];
+  // Activations of the next table travel through LDS: waves 0 and 1 load a
+  // slice (one byte position per lane) into registers, store it to the free
+  // half of `xstage` once the current lookups are issued, and every wave
+  // reads its 8 values from there when it builds the table.
+  const bool x_loader = wave < 2;
+  const int my_slot = 64 * (wave & 1) + lane;
+  float4 xn0 = make_float4(0.f, 0.f, 0.f, 0.f), xn1 = xn0;
+  int xb = 0;                                   // xstage half of the current step
+  if (x_loader) {
+    const int64_t rb = u_begin / sc.S;
+    load_x(ares, K, 0, static_cast<int>(u_begin - rb * sc.S), my_pos, xn0, xn1);
+  }
+#pragma unroll
+  for (int k = 0; k + 1 < DEPTH; ++k) load_unit(u_begin + k, wbuf[k]);
+  if (x_loader) {
+    xstage[0][2 * my_slot] = xn0;
+    xstage[0][2 * my_slot + 1] = xn1;
+  }
+
+  // One unit: its weights are in `cur`; the weights DEPTH - 1 units ahead go
+  // to `ahead`, so DEPTH - 1 units of loads stay in flight behind this one.
+  // Steps past the end (active == false) still issue their (empty) loads and
+  // register moves, so every pass of the unrolled loop has the same register
+  // flow and the compiler never has to drain the loads in flight.
+  auto do_unit = [&](int64_t u, bool active, const uint4* cur, uint4* ahead) {
+    const int64_t rb = u / sc.S;
+    const int sl = static_cast<int>(u - rb * sc.S);
+    const int j_lo = (u == u_begin) ? static_cast<int>(g_begin - u * JR) : 0;
+    const int j_hi = (u == u_last) ? static_cast<int>(g_end - u * JR) : JR;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if (t < B) {
-        // next step's activations first, then the next slice's weights
-        const bool last_tok = (t + 1 >= B) || (t + 1 >= NT);
-        if (!last_tok) load_x(ah + (int64_t)(t + 1) * K, K, sl, lane, xn0, xn1);
-        else if (sl + 1 < sl1) load_x(ah, K, sl + 1, lane, xn0, xn1);
-        if (t == 0 && sl + 1 < sl1) load_w(sl + 1, wn);
-        __syncthreads();                       // previous readers of the table are done
-        build_table(table, xc0, xc1, wave, lane);
+      // next step's activations (loader waves), then once per unit the
+      // weights DEPTH - 1 units on
+      if (x_loader) {
+        if (t + 1 < B && t + 1 < NT) {
+          load_x(ares, K, t + 1, active ? sl : sc.S, my_pos, xn0, xn1);
+        } else {
+          const int64_t un = u + 1;
+          const int64_t rbn = un / sc.S;
+          load_x(ares, K, 0, un <= u_last ? static_cast<int>(un - rbn * sc.S) : sc.S, my_pos,
+                 xn0, xn1);
+        }
+      }
+      if (t == 0) load_unit(u + DEPTH - 1, ahead);
+      if (active && t < B) {
+        __syncthreads();                       // table readers done, xstage[xb] written
+        const float4 xc0 = xstage[xb][2 * my_slot];
+        const float4 xc1 = xstage[xb][2 * my_slot + 1];
+        build_table<kWaves>(table, xc0, xc1, wave, lane);
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < JR; ++j) {
-          float a0 = *reinterpret_cast<const float*>(
-              tb + __builtin_amdgcn_perm(wv[j].x, lc[0], sel[0]));
-          float a1 = *reinterpret_cast<const float*>(
-              tb + __builtin_amdgcn_perm(wv[j].y, lc[1], sel[0]));
+          if (j >= j_lo && j < j_hi) {
+            const uint32_t wd[4] = {cur[j].x, cur[j].y, cur[j].z, cur[j].w};
+            float a[4];
 #pragma unroll
-          for (int i = 1; i < 4; ++i) {
-            a0 += *reinterpret_cast<const float*>(tb + __builtin_amdgcn_perm(wv[j].x, lc[0], sel[i]));
-            a1 += *reinterpret_cast<const float*>(tb + __builtin_amdgcn_perm(wv[j].y, lc[1], sel[i]));
+            for (int d = 0; d < 4; ++d)
+              a[d] = *reinterpret_cast<const float*>(tb + __builtin_amdgcn_perm(wd[d], lc[d][0],
+                                                                               sel[0]));
+#pragma unroll
+            for (int i = 1; i < 4; ++i)
+#pragma unroll
+              for (int d = 0; d < 4; ++d)
+                a[d] += *reinterpret_cast<const float*>(
+                    tb + __builtin_amdgcn_perm(wd[d], lc[d][i], sel[i]));
+            acc[t][j] += (a[0] + a[1]) + (a[2] + a[3]);
           }
-          acc[t][j] += a0 + a1;
         }
-        xc0 = xn0;
-        xc1 = xn1;
+        xb ^= 1;
+      }
+      // the other half was last read before this step's second barrier
+      if (x_loader) {
+        xstage[xb][2 * my_slot] = xn0;
+        xstage[xb][2 * my_slot + 1] = xn1;
       }
     }
-#pragma unroll
-    for (int j = 0; j < JR; ++j) wv[j] = wn[j];
-  }
+    if (active && (u == u_last || (u + 1) / sc.S != rb)) flush(rb);
+  };
 
-  // reduce the 8 lanes of each row; lane c == 0 holds the row's partial sum
+  for (int64_t u = u_begin; u <= u_last; u += DEPTH) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int j = 0; j < JR; ++j) acc[t][j] = sum8(acc[t][j]);
-
-  if (parts == 1) {
-    if (c == 0) {
-#pragma unroll
-      for (int j = 0; j < JR; ++j) {
-        const int64_t row = row0 + (j * kWaves + wave) * 8 + rsub;
-        if (row < m) {
-          const float sc = s[row];
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-            if (t < B) out[(int64_t)t * m + row] = sc * acc[t][j];
-        }
-      }
-    }
-    return;
+    for (int k = 0; k < DEPTH; ++k)
+      do_unit(u + k, u + k <= u_last, wbuf[k], wbuf[(k + DEPTH - 1) % DEPTH]);
   }
-
-  if (c == 0) {
-#pragma unroll
-    for (int j = 0; j < JR; ++j) {
-      const int64_t row = row0 + (j * kWaves + wave) * 8 + rsub;
-      if (row < m) {
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-          if (t < B) partials[((int64_t)part * B + t) * m + row] = acc[t][j];
-      }
-    }
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned prev =
-        __hip_atomic_fetch_add(&counters[rb], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (prev == static_cast<unsigned>(parts - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const int64_t nrows = (m - row0) < R ? (m - row0) : R;
-  for (int64_t i = tid; i < nrows * B; i += kThreads) {
-    const int t = static_cast<int>(i / nrows);
-    const int64_t row = row0 + (i - (int64_t)t * nrows);
-    float sum = 0.f;
-    for (int p = 0; p < parts; ++p)
-      sum += __hip_atomic_load(&partials[((int64_t)p * B + t) * m + row], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    out[(int64_t)t * m + row] = s[row] * sum;
-  }
-  if (tid == 0)
-    __hip_atomic_store(&counters[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Rows per workgroup are 64*JR.  JR = 8 keeps every variant under 128 VGPRs,
-// so two 512-thread workgroups (64 KB of table each) share a CU.
-constexpr int kMaxJR = 8;
+int g_num_cus[64] = {0};
+
+int num_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (g_num_cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    g_num_cus[dev] = n;
+  }
+  return g_num_cus[dev];
+}
+
+constexpr int kUnitRows = 512;                  // rows per unit
+constexpr int kGemvThreads = 1024;              // 16 waves: 4 per SIMD
+constexpr int kJR = kUnitRows / (kGemvThreads / 8);
+
+Sched make_sched(int64_t m, int64_t K, int jr, int G, int rows_per_step = kGemvThreads / 8) {
+  Sched sc{};
+  const int64_t R = (int64_t)rows_per_step * jr;
+  sc.S = static_cast<int>((K + kSliceBits - 1) / kSliceBits);
+  sc.rbs = static_cast<int>((m + R - 1) / R);
+  sc.T = (int64_t)sc.rbs * sc.S * jr;
+  sc.G = static_cast<int>(sc.T < G ? sc.T : G);
+  int kmax = 1;
+  for (int rb = 0; rb < sc.rbs; ++rb) {
+    const int64_t g0 = (int64_t)rb * sc.S * jr;
+    const int n = owner(g0 + (int64_t)sc.S * jr - 1, sc.T, sc.G) - owner(g0, sc.T, sc.G) + 1;
+    if (n > kmax) kmax = n;
+  }
+  sc.kmax = kmax;
+  return sc;
+}
+
+
+// ============================================================================
+// Batch-1 kernel on prebuilt float16 tables (k_lut.hip builds them once per
+// call, shared by every workgroup).  Same persistent stream-K split as above,
+// with 1024-row units; per unit the workgroup pulls the slice's 64 KB table
+// straight into LDS with buffer loads to LDS (no registers, no table-building
+// arithmetic), double-buffered so the next table and the next unit's weights
+// stream in while the current unit's lookups run: one barrier per unit.
+// A lookup is one v_perm_b32 (address) + one ds_read_u16 + one v_fma_mix_f32
+// (the float16 entry added in float32).
+// ============================================================================
+constexpr int kV3Threads = 1024;               // 16 waves, 4 per SIMD
+constexpr int kV3Waves = kV3Threads / 64;
+constexpr int kV3RowsPerStep = kV3Waves * 8;   // 128
+constexpr int kV3JR = 4;                       // 512-row units
+constexpr int kV3R = kV3RowsPerStep * kV3JR;
+
+__device__ __forceinline__ float add_f16_lo(float acc, uint32_t h) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(acc));
+  return r;
+}
+
+__global__ void __launch_bounds__(kV3Threads, 1) gemv1_lut_kernel(
+    const uint32_t* __restrict__ w, int64_t m, int64_t ldw, const float* __restrict__ s,
+    const uint16_t* __restrict__ lut, float* __restrict__ out, float* __restrict__ partials,
+    unsigned* __restrict__ counters, Sched sc, uint32_t w_bytes, uint32_t lut_bytes) {
+  __shared__ __attribute__((aligned(16))) unsigned char tabs[2 * 65536];
+  __shared__ int s_last;
+
+  constexpr int JR = kV3JR;
+  constexpr int R = kV3R;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wg = blockIdx.x;
+  const int64_t g_begin = (int64_t)wg * sc.T / sc.G;
+  const int64_t g_end = (int64_t)(wg + 1) * sc.T / sc.G;
+  if (g_begin >= g_end) return;
+  const int64_t u_begin = g_begin / JR;
+  const int64_t u_last = (g_end - 1) / JR;
+
+  const int r = lane >> 3;
+  const int c = lane & 7;
+  const int r4 = r & 3;
+  // address = 65536 * buffer + 256 * weight byte + 2 * slot: byte 0 from the
+  // lane constant (2 * slot), byte 1 the weight byte, byte 2 the buffer
+  // (0 from the selector's zero, 1 from the lane constant's byte 2)
+  uint32_t lc[4][4];
+  uint32_t selb[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t b = (i + r4) & 3;
+    selb[0][i] = 0u | ((4u + b) << 8) | (0x0Cu << 16) | (0x0Cu << 24);
+    selb[1][i] = 0u | ((4u + b) << 8) | (0x02u << 16) | (0x0Cu << 24);
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      lc[d][i] = static_cast<uint32_t>(2 * lut_slot(16 * c + 4 * d + static_cast<int>(b))) |
+                 (1u << 16);
+  }
+
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(w), (short)0, static_cast<int>(w_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t lres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(lut), (short)0, static_cast<int>(lut_bytes), 0x00020000);
+  const uint32_t row_bytes = static_cast<uint32_t>(ldw * 4);
+
+  auto load_unit = [&](int64_t u, uint4* wv) {
+    const bool ok = u <= u_last;
+    const int64_t rb = u / sc.S;
+    const int sl = static_cast<int>(u - rb * sc.S);
+    const int j_lo = (ok && u == u_begin) ? static_cast<int>(g_begin - u * JR) : 0;
+    const int j_hi = (ok && u == u_last) ? static_cast<int>(g_end - u * JR) : JR;
+    const uint32_t base = static_cast<uint32_t>(
+        (rb * R + wave * 8 + r) * (int64_t)row_bytes + (int64_t)sl * kSliceBytes + 16 * c);
+#pragma unroll
+    for (int j = 0; j < JR; ++j) {
+      const uint32_t off = (ok && j >= j_lo && j < j_hi)
+                               ? base + static_cast<uint32_t>(j * kV3RowsPerStep) * row_bytes
+                               : kNoLoad;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, 0);
+      __builtin_memcpy(&wv[j], &v, 16);
+    }
+  };
+  // 64 KB table of unit u into LDS buffer `buf`: 4 loads of 16 bytes per lane
+  auto load_table = [&](int64_t u, int buf) {
+    const bool ok = u <= u_last;
+    const int sl = static_cast<int>(u - (u / sc.S) * sc.S);
+    const uint32_t soff = ok ? static_cast<uint32_t>(sl) * 65536u : kNoLoad;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int chunk = k * kV3Waves + wave;                       // 1 KB per wave
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          lres, (__attribute__((address_space(3))) void*)(tabs + buf * 65536 + chunk * 1024), 16,
+          static_cast<uint32_t>(chunk * 1024 + lane * 16), soff, 0, 0);
+    }
+  };
+
+  float acc[JR];
+#pragma unroll
+  for (int j = 0; j < JR; ++j) acc[j] = 0.f;
+
+  auto flush = [&](int64_t rb) {
+#pragma unroll
+    for (int j = 0; j < JR; ++j) acc[j] = sum8(acc[j]);
+    const int64_t g0 = rb * sc.S * JR;
+    const int w_first = owner(g0, sc.T, sc.G);
+    const int w_last = owner(g0 + (int64_t)sc.S * JR - 1, sc.T, sc.G);
+    const int n = w_last - w_first + 1;
+    if (n == 1) {
+      if (c == 0) {
+#pragma unroll
+        for (int j = 0; j < JR; ++j) {
+          const int64_t row = rb * R + j * kV3RowsPerStep + wave * 8 + r;
+          if (row < m) out[row] = s[row] * acc[j];
+        }
+      }
+    } else {
+      const int k = wg - w_first;
+      float* pb = partials + (rb * sc.kmax + k) * (int64_t)R;
+      if (c == 0) {
+#pragma unroll
+        for (int j = 0; j < JR; ++j)
+          __hip_atomic_store(pb + j * kV3RowsPerStep + wave * 8 + r, acc[j], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (tid == 0) {
+        const unsigned prev = __hip_atomic_fetch_add(&counters[rb], 1u, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == static_cast<unsigned>(n - 1)) ? 1 : 0;
+      }
+      __syncthreads();
+      if (s_last) {
+        const float* p0 = partials + rb * sc.kmax * (int64_t)R;
+        for (int rr = tid; rr < R; rr += kV3Threads) {
+          const int64_t row = rb * R + rr;
+          if (row < m) {
+            float sum = 0.f;
+            for (int k0 = 0; k0 < n; k0 += 8) {
+              float v[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                v[e] = (k0 + e < n) ? __hip_atomic_load(p0 + (int64_t)(k0 + e) * R + rr,
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                    : 0.f;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) sum += v[e];
+            }
+            out[row] = s[row] * sum;
+          }
+        }
+        if (tid == 0)
+          __hip_atomic_store(&counters[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < JR; ++j) acc[j] = 0.f;
+  };
+
+  uint4 wbuf[2][JR];
+  load_table(u_begin, 0);
+  load_unit(u_begin, wbuf[0]);
+
+  // One unit in buffer `buf`: wait for its table (issued one unit earlier,
+  // ahead of its weights), then request the next unit's table and weights,
+  // then look up.  Steps past the end still issue their (empty) loads so the
+  // unrolled loop's register flow never changes.
+  auto do_unit = [&](int64_t u, bool active, int buf, const uint4* cur, uint4* nxt) {
+    const int64_t rb = u / sc.S;
+    const int j_lo = (u == u_begin) ? static_cast<int>(g_begin - u * JR) : 0;
+    const int j_hi = (u == u_last) ? static_cast<int>(g_end - u * JR) : JR;
+    // outstanding here, oldest first: this table (4), this unit's weights (JR)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (JR & 15) | ((JR >> 4) << 14));
+    __syncthreads();                    // every wave's part of the table landed;
+                                        // the other buffer is no longer read
+    load_table(u + 1, buf ^ 1);
+    load_unit(u + 1, nxt);
+    if (active) {
+      const char* tb = reinterpret_cast<const char*>(tabs);
+#pragma unroll
+      for (int j = 0; j < JR; ++j) {
+        if (j >= j_lo && j < j_hi) {
+          const uint32_t wd[4] = {cur[j].x, cur[j].y, cur[j].z, cur[j].w};
+          float a = acc[j];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              const uint32_t ad = __builtin_amdgcn_perm(wd[d], lc[d][i], selb[buf][i]);
+              a = add_f16_lo(a, *reinterpret_cast<const uint16_t*>(tb + ad));
+            }
+          acc[j] = a;
+        }
+      }
+      if (u == u_last || (u + 1) / sc.S != rb) flush(rb);
+    }
+  };
+
+  for (int64_t u = u_begin; u <= u_last; u += 2) {
+    do_unit(u, true, 0, wbuf[0], wbuf[1]);
+    do_unit(u + 1, u + 1 <= u_last, 1, wbuf[1], wbuf[0]);
+  }
+}
 
 }  // namespace
 
+size_t gemv_counter_bytes(int64_t m) {
+  // one arrival counter per row block (row blocks are >= 64 rows)
+  return ((size_t)((m + 63) / 64) * sizeof(unsigned) + 255) / 256 * 256;
+}
+
 GemvPlan plan_gemv(int64_t m, int64_t K, int64_t B) {
   GemvPlan p{};
-  p.slices = static_cast<int>((K + kSliceBits - 1) / kSliceBits);
-  const int target = 512;                       // 2 workgroups per CU
-  // Largest row block that still leaves enough workgroups once K is split.
-  int best_jr = 1, best_spp = 1;
-  double best_cost = 1e300;
-  for (int jr = 1; jr <= kMaxJR; jr *= 2) {
-    const int64_t R = 64 * jr;
-    const int64_t rbs = (m + R - 1) / R;
-    for (int spp = 1; spp <= p.slices; ++spp) {
-      const int64_t parts = (p.slices + spp - 1) / spp;
-      const int64_t nwg = rbs * parts;
-      const int64_t rounds = (nwg + target - 1) / target;
-      // cost per workgroup in "bytes of HBM time": weights + table builds
-      // (about 6.5 KB each) + partial sums written and read back.
-      const double wg = (double)R * spp * 64.0 + (double)spp * B * 6656.0 +
-                        (parts > 1 ? (double)R * B * 8.0 : 0.0);
-      const double cost = rounds * wg;
-      if (cost < best_cost * 0.999) {
-        best_cost = cost;
-        best_jr = jr;
-        best_spp = spp;
-      }
-    }
-  }
-  p.rows_per_wg = 64 * best_jr;
-  p.slices_per_part = best_spp;
-  p.parts = (p.slices + best_spp - 1) / best_spp;
-  p.row_blocks = static_cast<int>((m + p.rows_per_wg - 1) / p.rows_per_wg);
+  const int nt = B <= 1 ? 1 : B <= 2 ? 2 : 4;
+  const Sched sc = make_sched(m, K, kJR, num_cus());
+  p.rows_per_wg = kUnitRows;
+  p.slices = sc.S;
+  p.row_blocks = sc.rbs;
+  p.parts = sc.kmax;
+  p.slices_per_part = 0;
   p.ws_bytes = 0;
-  if (p.parts > 1)
-    p.ws_bytes = gemv_counter_bytes(m) + sizeof(float) * (size_t)p.parts * (size_t)B * (size_t)m;
+  if (sc.kmax > 1)
+    p.ws_bytes = gemv_counter_bytes(m) +
+                 sizeof(float) * (size_t)sc.rbs * sc.kmax * nt * (size_t)p.rows_per_wg;
   return p;
 }
 
-size_t gemv_counter_bytes(int64_t m) {
-  // one arrival counter per possible row block (row blocks are >= 64 rows)
-  return ((size_t)((m + 63) / 64) * sizeof(unsigned) + 255) / 256 * 256;
+// Workspace of the batch-1 path: [arrival counters][partial sums][tables].
+size_t gemv1_lut_offset(int64_t m, int64_t K) {
+  const Sched sc = make_sched(m, K, kV3JR, num_cus(), kV3RowsPerStep);
+  size_t b = gemv_counter_bytes(m);
+  if (sc.kmax > 1) b += ((sizeof(float) * (size_t)sc.rbs * sc.kmax * kV3R) + 255) / 256 * 256;
+  return b;
 }
+
+size_t gemv1_workspace_bytes(int64_t m, int64_t K) {
+  return gemv1_lut_offset(m, K) + static_cast<size_t>(lut_bytes(1, K));
+}
+
+hipError_t launch_gemv1_lut(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
+                            const void* lut, float* out, void* ws, hipStream_t st) {
+  const Sched sc = make_sched(m, K, kV3JR, num_cus(), kV3RowsPerStep);
+  unsigned* counters = static_cast<unsigned*>(ws);
+  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + gemv_counter_bytes(m));
+  hipLaunchKernelGGL(gemv1_lut_kernel, dim3(sc.G), dim3(kV3Threads), 0, st, w, m, ldw, s,
+                     static_cast<const uint16_t*>(lut), out, partials, counters, sc,
+                     static_cast<uint32_t>(m * ldw * 4), static_cast<uint32_t>(lut_bytes(1, K)));
+  return hipGetLastError();
+}
+
 
 size_t gemv_workspace_bytes(int64_t m, int64_t K, int64_t B) {
   size_t mx = 0;
@@ -316,43 +665,33 @@ size_t gemv_workspace_bytes(int64_t m, int64_t K, int64_t B) {
   return mx;
 }
 
-template <int NT, int JR>
-static hipError_t launch_t(const GemvPlan& p, const uint32_t* w, int64_t m, int64_t K,
-                           int64_t ldw, const float* s, const float* ah, int64_t B, float* out,
-                           void* ws, hipStream_t st) {
-  // workspace: [arrival counters][partial sums]; counters stay zero between calls
+template <int NT>
+static hipError_t launch_nt(const uint32_t* w, int64_t m, int64_t K, int64_t ldw,
+                            const float* s, const float* ah, int64_t B, float* out, void* ws,
+                            hipStream_t st) {
+  const Sched sc = make_sched(m, K, kJR, num_cus());
   unsigned* counters = nullptr;
   float* partials = nullptr;
-  if (p.parts > 1) {
+  if (sc.kmax > 1) {
     counters = static_cast<unsigned*>(ws);
     partials = reinterpret_cast<float*>(static_cast<char*>(ws) + gemv_counter_bytes(m));
   }
-  hipLaunchKernelGGL((gemv_lut_kernel<NT, JR>), dim3(p.row_blocks * p.parts), dim3(kThreads), 0,
-                     st, w, m, K, ldw, s, ah, static_cast<int>(B), out, partials, counters,
-                     p.slices_per_part, p.parts, p.slices,
-                     static_cast<uint32_t>(m * ldw * 4));
+  // two units in flight for one token; with more tokens the per-unit work
+  // hides the latency with one (and the registers go to accumulators)
+  constexpr int DEPTH = 2;
+  hipLaunchKernelGGL((gemv_lut_kernel<kGemvThreads, NT, kJR, DEPTH>), dim3(sc.G),
+                     dim3(kGemvThreads), 0, st, w, m, K, ldw,
+                     s, ah, static_cast<int>(B), out, partials, counters, sc,
+                     static_cast<uint32_t>(m * ldw * 4), static_cast<uint32_t>(B * K * 4));
   return hipGetLastError();
 }
 
-template <int NT>
-static hipError_t launch_nt(const GemvPlan& p, const uint32_t* w, int64_t m, int64_t K,
-                            int64_t ldw, const float* s, const float* ah, int64_t B, float* out,
-                            void* ws, hipStream_t st) {
-  switch (p.rows_per_wg / 64) {
-    case 1: return launch_t<NT, 1>(p, w, m, K, ldw, s, ah, B, out, ws, st);
-    case 2: return launch_t<NT, 2>(p, w, m, K, ldw, s, ah, B, out, ws, st);
-    case 4: return launch_t<NT, 4>(p, w, m, K, ldw, s, ah, B, out, ws, st);
-    case 8: return launch_t<NT, 8>(p, w, m, K, ldw, s, ah, B, out, ws, st);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-hipError_t launch_gemv(const GemvPlan& p, const uint32_t* w, int64_t m, int64_t K, int64_t ldw,
+hipError_t launch_gemv(const GemvPlan&, const uint32_t* w, int64_t m, int64_t K, int64_t ldw,
                        const float* s, const float* ah, int64_t B, float* out, void* ws,
                        hipStream_t st) {
-  if (B <= 1) return launch_nt<1>(p, w, m, K, ldw, s, ah, B, out, ws, st);
-  if (B <= 2) return launch_nt<2>(p, w, m, K, ldw, s, ah, B, out, ws, st);
-  if (B <= 4) return launch_nt<4>(p, w, m, K, ldw, s, ah, B, out, ws, st);
+  if (B <= 1) return launch_nt<1>(w, m, K, ldw, s, ah, B, out, ws, st);
+  if (B <= 2) return launch_nt<2>(w, m, K, ldw, s, ah, B, out, ws, st);
+  if (B <= 4) return launch_nt<4>(w, m, K, ldw, s, ah, B, out, ws, st);
   return hipErrorInvalidValue;
 }
 

@@ -115,7 +115,7 @@ lq_status lq_gemv_workspace_size(int64_t m, int64_t K, int64_t B, size_t* bytes)
   if (!bytes) return fail(LQ_ERR_NULL, "bytes is null");
   if (m < 1 || K < 1 || B < 1 || B > 16)
     return fail(LQ_ERR_SHAPE, "m=%lld K=%lld B=%lld", (long long)m, (long long)K, (long long)B);
-  *bytes = lq::gemv_workspace_bytes(m, K, B);
+  *bytes = B == 1 ? lq::gemv1_workspace_bytes(m, K) : lq::gemv_workspace_bytes(m, K, B);
   return ok();
 }
 
@@ -134,20 +134,31 @@ lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw, c
   if (m < 1 || K < 1) return fail(LQ_ERR_SHAPE, "m=%lld K=%lld", (long long)m, (long long)K);
   if (B < 1 || B > 16) return fail(LQ_ERR_SHAPE, "B=%lld outside 1..16", (long long)B);
   if (ldw < (K + 31) / 32) return fail(LQ_ERR_SHAPE, "ldw=%lld < ceil(K/32)", (long long)ldw);
-  if (ldw % 2) return fail(LQ_ERR_ALIGN, "ldw=%lld must be even", (long long)ldw);
+  if (ldw % 4) return fail(LQ_ERR_ALIGN, "ldw=%lld must be a multiple of 4", (long long)ldw);
   if (K % 4) return fail(LQ_ERR_SHAPE, "K=%lld must be a multiple of 4", (long long)K);
-  if (m * ldw * 4 > (int64_t)UINT32_MAX)
-    return fail(LQ_ERR_SHAPE, "weights of %lld bytes exceed the 4 GiB per-call limit",
+  // the kernel addresses weights and activations with 32-bit buffer offsets
+  if (m * ldw * 4 > ((int64_t)1 << 30))
+    return fail(LQ_ERR_SHAPE, "weights of %lld bytes exceed the 1 GiB per-call limit",
                 (long long)(m * ldw * 4));
-  if (!aligned(w_packed, 8)) return fail(LQ_ERR_ALIGN, "w_packed must be 8-byte aligned");
+  if (K > ((int64_t)1 << 24))
+    return fail(LQ_ERR_SHAPE, "K=%lld exceeds the per-call limit of 2^24", (long long)K);
+  if (!aligned(w_packed, 16)) return fail(LQ_ERR_ALIGN, "w_packed must be 16-byte aligned");
   if (!aligned(a_lift, 16)) return fail(LQ_ERR_ALIGN, "a_lift must be 16-byte aligned");
   if (!aligned(s, 4) || !aligned(out, 4)) return fail(LQ_ERR_ALIGN, "misaligned s or out");
-  const size_t need = lq::gemv_workspace_bytes(m, K, B);
+  const size_t need = B == 1 ? lq::gemv1_workspace_bytes(m, K) : lq::gemv_workspace_bytes(m, K, B);
   if (need > 0) {
     if (!workspace) return fail(LQ_ERR_WORKSPACE, "workspace of %zu bytes required", need);
     if (workspace_bytes < need)
       return fail(LQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
     if (!aligned(workspace, 256)) return fail(LQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+  }
+  if (B == 1) {
+    // one token: float16 activation-sum tables, then the table-driven kernel
+    void* lut = static_cast<char*>(workspace) + lq::gemv1_lut_offset(m, K);
+    hipError_t e = lq::launch_build_lut(a_lift, 1, K, lut, as_stream(stream));
+    if (e == hipSuccess)
+      e = lq::launch_gemv1_lut(w_packed, m, K, ldw, s, lut, out, workspace, as_stream(stream));
+    return hip_status(e, "lq_gemv launch");
   }
   // Tokens go through in groups of at most 4; each group rereads the weights.
   for (int64_t t0 = 0; t0 < B; t0 += 4) {

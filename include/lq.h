@@ -123,16 +123,18 @@ lq_status lq_workspace_clear(void* workspace, size_t bytes, void* stream);
  *   out[b][i] = s[i] * sum_{k<K} sigma_ik * a_lift[b][k],
  *   sigma_ik = +1 if bit k of row i is 1, else -1.
  * w_packed: uint32 [m][ldw] (layout of lq_pack_signs), ldw >= ceil(K/32),
- *           ldw even and w_packed 8-byte aligned.
+ *           ldw a multiple of 4 and w_packed 16-byte aligned (16-byte loads).
  * s:        float [m].
  * a_lift:   float [B][K] (lq_lift_activations with LQ_F32), 16-byte aligned,
  *           K % 4 == 0.
  * out:      float [B][m].
  * workspace: device buffer of >= lq_gemv_workspace_size bytes, cleared once
  *           (lq_workspace_clear); may be NULL when that size is 0.
- * Requires 1 <= B <= 16, m >= 1, K >= 1.  Accumulation is float32; the
- * result does not depend on the launch configuration's timing (no float
- * atomics).
+ * Requires 1 <= B <= 16, m >= 1, K >= 1, m*ldw*4 <= 2^30 bytes (split
+ * larger matrices by rows over several calls) and K <= 2^24.  Accumulation is
+ * float32; the result does not depend on timing (no float atomics).  With
+ * B == 1 the activation sums are rounded to float16 before the float32
+ * accumulation (relative output error ~3e-4); with B >= 2 they stay float32.
  */
 lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw,
                   const float* s, const float* a_lift, int64_t B, float* out,

@@ -51,16 +51,18 @@ def _err(L):
 
 def test_gemv_validation(L):
     ws = 0
-    assert L.lq_gemv(None, 8, 64, 2, P, P, 1, P, None, ws, None) == 1       # null weights
-    assert L.lq_gemv(P, 8, 64, 2, P, P, 0, P, None, ws, None) == 2          # B = 0
-    assert L.lq_gemv(P, 8, 64, 2, P, P, 17, P, None, ws, None) == 2         # B > 16
+    assert L.lq_gemv(None, 8, 64, 4, P, P, 1, P, None, ws, None) == 1       # null weights
+    assert L.lq_gemv(P, 8, 64, 4, P, P, 0, P, None, ws, None) == 2          # B = 0
+    assert L.lq_gemv(P, 8, 64, 4, P, P, 17, P, None, ws, None) == 2         # B > 16
     assert "1..16" in _err(L)
     assert L.lq_gemv(P, 8, 64, 1, P, P, 1, P, None, ws, None) == 2          # ldw < K/32
-    assert L.lq_gemv(P, 8, 96, 3, P, P, 1, P, None, ws, None) == 4          # odd ldw
+    assert L.lq_gemv(P, 8, 96, 3, P, P, 1, P, None, ws, None) == 4          # ldw % 4
+    assert L.lq_gemv(P, 8, 96, 6, P, P, 1, P, None, ws, None) == 4
     assert L.lq_gemv(P, 8, 66, 4, P, P, 1, P, None, ws, None) == 2          # K % 4
-    assert L.lq_gemv(MIS, 8, 64, 2, P, P, 1, P, None, ws, None) == 4        # misaligned w
-    assert L.lq_gemv(P, 8, 64, 2, P, MIS, 1, P, None, ws, None) == 4       # misaligned a_lift
-    assert L.lq_gemv(P, 0, 64, 2, P, P, 1, P, None, ws, None) == 2          # m = 0
+    assert L.lq_gemv(P + 8, 8, 64, 4, P, P, 1, P, None, ws, None) == 4      # w not 16B-aligned
+    assert L.lq_gemv(MIS, 8, 64, 4, P, P, 1, P, None, ws, None) == 4        # misaligned w
+    assert L.lq_gemv(P, 8, 64, 4, P, MIS, 1, P, None, ws, None) == 4       # misaligned a_lift
+    assert L.lq_gemv(P, 0, 64, 4, P, P, 1, P, None, ws, None) == 2          # m = 0
 
 
 def test_gemv_workspace_required(L):
@@ -112,7 +114,7 @@ def test_gemm_and_pack_validation(L):
 
 def test_error_message_is_thread_local_and_cleared(L):
     import threading
-    assert L.lq_gemv(None, 8, 64, 2, P, P, 1, P, None, 0, None) == 1
+    assert L.lq_gemv(None, 8, 64, 4, P, P, 1, P, None, 0, None) == 1
     seen = {}
 
     def other():

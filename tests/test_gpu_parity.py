@@ -22,6 +22,11 @@ pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
 TOL_F32 = 1e-4
+# One token: the activation sums (8 terms each) are rounded to float16 (half
+# an ulp = 2^-11 relative) and then added in float32.  Independent rounding
+# errors give a relative output error of about 2^-11/sqrt(3) ~ 3e-4 in both
+# the largest error and the largest output; 1e-3 keeps a 3x margin.
+TOL_LUT16 = 1e-3
 
 
 @pytest.fixture(scope="module")
@@ -103,7 +108,7 @@ GEMV_CASES = [  # (m, K, B): ragged rows, slices and token groups
 def test_gemv_lifted_product(dev, m, K, B):
     _banner(f"gemv m={m} K={K} B={B}")
     rng = np.random.default_rng(m * 7 + K + B)
-    ldw = ((K + 31) // 32 + 1) // 2 * 2
+    ldw = ((K + 31) // 32 + 3) // 4 * 4
     packed = synth.random_sign_words(rng, m, K, ldw=ldw)
     al = rng.standard_normal((B, K)).astype(np.float32)
     s = rng.uniform(0.01, 0.03, m).astype(np.float32)
@@ -111,7 +116,7 @@ def test_gemv_lifted_product(dev, m, K, B):
     got = lq.gemv(torch.from_numpy(packed.view(np.int32)).to(dev), torch.from_numpy(s).to(dev),
                   torch.from_numpy(al).to(dev), K).cpu().numpy()
     e = O.rel_err_colmax(got, ref)
-    assert e <= TOL_F32, e
+    assert e <= (TOL_LUT16 if B == 1 else TOL_F32), e
 
 
 def test_gemv_deterministic(dev):
@@ -207,7 +212,9 @@ def test_layer_small(dev, m, n, d, D, B, dt):
     got = dl.forward(_up(L.a, dt, dev)).cpu().numpy()
     e = O.rel_err_colmax(got, ref)
     assert e <= TOL, e
-    if B <= 16:
+    if B == 1:
+        assert e <= TOL_LUT16, e
+    elif B <= 16:
         assert e <= TOL_F32, e
 
 
