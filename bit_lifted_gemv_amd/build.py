@@ -19,12 +19,15 @@ ARCH = "gfx950"
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
     "-fPIC",
     "-Wall",
     "-Wno-unused-function",
     # packed fp32 instructions are kept out of the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # one lane issues each arrival-counter increment; the wave-wide atomic
+    # rewrite would wait for the result at once and drain the load stream
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
 ]
 
 

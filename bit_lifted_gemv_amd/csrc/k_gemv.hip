@@ -30,84 +30,10 @@
 // one partial sum per workgroup in the workspace, and the last of them to
 // arrive (arrival counter) adds them in workgroup order, so the result is
 // deterministic.
-#include "lq_internal.h"
+#include "lut_common.h"
 
 namespace lq {
 namespace {
-
-constexpr int kSliceBits = 1024;
-constexpr int kSliceBytes = kSliceBits / 8;    // 128
-constexpr int kTableFloats = 128 * 256;        // 128 KB
-constexpr uint32_t kNoLoad = 0x80000000u;      // outside every buffer resource
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_add(float v) {
-  const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false);
-  return v + __int_as_float(o);
-}
-
-// Sum over the 8 lanes of an aligned lane group; every lane gets the total.
-__device__ __forceinline__ float sum8(float v) {
-  v = dpp_add<0xB1>(v);    // quad_perm [1,0,3,2]
-  v = dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]
-  v = dpp_add<0x141>(v);   // row_half_mirror
-  return v;
-}
-
-__host__ __device__ constexpr int gray(int i) { return i ^ (i >> 1); }
-__host__ __device__ constexpr int ctz6(int i) {
-  return (i & 1) ? 0 : (i & 2) ? 1 : (i & 4) ? 2 : (i & 8) ? 3 : (i & 16) ? 4 : 5;
-}
-
-// Slot of byte position p (and back: the map is an involution).  Byte b of
-// dword d of 16-byte chunk c: p = 16c + 4d + b -> 16c + 4(d ^ (c >> 1)) + b.
-__host__ __device__ constexpr int slot_of(int p) {
-  return (p & ~12) | ((((p >> 2) & 3) ^ ((p >> 5) & 3)) << 2);
-}
-
-// Activations of byte position p of slice sl for token t (zero past K).
-__device__ __forceinline__ void load_x(__amdgpu_buffer_rsrc_t ares, int64_t K, int t, int sl,
-                                       int p, float4& x0, float4& x1) {
-  const int64_t k0 = (int64_t)sl * kSliceBits + 8 * p;
-  const uint32_t base = static_cast<uint32_t>(((int64_t)t * K + k0) * 4);
-  const uint32_t o0 = (k0 + 4 <= K) ? base : kNoLoad;
-  const uint32_t o1 = (k0 + 8 <= K) ? base + 16 : kNoLoad;
-  const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(ares, o0, 0, 0);
-  const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(ares, o1, 0, 0);
-  __builtin_memcpy(&x0, &v0, 16);
-  __builtin_memcpy(&x1, &v1, 16);
-}
-
-// Table of one slice and token, built by WAVES waves.  Wave w: slot half
-// h = w & 1 (slots 64h .. 64h + 63, one per lane), entry block q = w >> 1
-// (v in [E*q, E*q + E), E = 512 / WAVES entries), low bits of v visited in
-// Gray-code order: one add per entry.
-template <int WAVES>
-__device__ __forceinline__ void build_table(float* __restrict__ table, const float4& x0,
-                                            const float4& x1, int wave, int lane) {
-  constexpr int E = 512 / WAVES;                 // entries per lane: 64 or 32
-  constexpr int LB = E == 64 ? 6 : 5;            // Gray-coded low bits
-  const int h = wave & 1;
-  const int q = wave >> 1;
-  const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-  float val = 0.f;
-#pragma unroll
-  for (int t = 0; t < LB; ++t) val -= x[t];
-#pragma unroll
-  for (int t = LB; t < 8; ++t) val += ((q >> (t - LB)) & 1) ? x[t] : -x[t];
-  float tw[LB];
-#pragma unroll
-  for (int t = 0; t < LB; ++t) tw[t] = 2.f * x[t];
-  float* base = table + h * 16384 + (E * q) * 64 + lane;
-  base[0] = val;
-#pragma unroll
-  for (int i = 1; i < E; ++i) {
-    const int t = ctz6(i);
-    const bool up = (gray(i) >> t) & 1;
-    val = up ? val + tw[t] : val - tw[t];
-    base[gray(i) * 64] = val;
-  }
-}
 
 struct Sched {
   int64_t T;        // 64-row steps in the iteration space (row blocks x slices x JR)
@@ -367,21 +293,6 @@ __global__ void __launch_bounds__(THREADS, 1) gemv_lut_kernel(
   }
 }
 
-int g_num_cus[64] = {0};
-
-int num_cus() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (g_num_cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        n <= 0)
-      n = 256;
-    g_num_cus[dev] = n;
-  }
-  return g_num_cus[dev];
-}
-
 constexpr int kUnitRows = 512;                  // rows per unit
 constexpr int kGemvThreads = 1024;              // 16 waves: 4 per SIMD
 constexpr int kJR = kUnitRows / (kGemvThreads / 8);
@@ -404,216 +315,30 @@ Sched make_sched(int64_t m, int64_t K, int jr, int G, int rows_per_step = kGemvT
 }
 
 
-// ============================================================================
-// Batch-1 kernel on prebuilt float16 tables (k_lut.hip builds them once per
-// call, shared by every workgroup).  Same persistent stream-K split as above,
-// with 1024-row units; per unit the workgroup pulls the slice's 64 KB table
-// straight into LDS with buffer loads to LDS (no registers, no table-building
-// arithmetic), double-buffered so the next table and the next unit's weights
-// stream in while the current unit's lookups run: one barrier per unit.
-// A lookup is one v_perm_b32 (address) + one ds_read_u16 + one v_fma_mix_f32
-// (the float16 entry added in float32).
-// ============================================================================
-constexpr int kV3Threads = 1024;               // 16 waves, 4 per SIMD
-constexpr int kV3Waves = kV3Threads / 64;
-constexpr int kV3RowsPerStep = kV3Waves * 8;   // 128
-constexpr int kV3JR = 4;                       // 512-row units
-constexpr int kV3R = kV3RowsPerStep * kV3JR;
-
-__device__ __forceinline__ float add_f16_lo(float acc, uint32_t h) {
-  float r;
-  asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(acc));
-  return r;
-}
-
-__global__ void __launch_bounds__(kV3Threads, 1) gemv1_lut_kernel(
-    const uint32_t* __restrict__ w, int64_t m, int64_t ldw, const float* __restrict__ s,
-    const uint16_t* __restrict__ lut, float* __restrict__ out, float* __restrict__ partials,
-    unsigned* __restrict__ counters, Sched sc, uint32_t w_bytes, uint32_t lut_bytes) {
-  __shared__ __attribute__((aligned(16))) unsigned char tabs[2 * 65536];
-  __shared__ int s_last;
-
-  constexpr int JR = kV3JR;
-  constexpr int R = kV3R;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wg = blockIdx.x;
-  const int64_t g_begin = (int64_t)wg * sc.T / sc.G;
-  const int64_t g_end = (int64_t)(wg + 1) * sc.T / sc.G;
-  if (g_begin >= g_end) return;
-  const int64_t u_begin = g_begin / JR;
-  const int64_t u_last = (g_end - 1) / JR;
-
-  const int r = lane >> 3;
-  const int c = lane & 7;
-  const int r4 = r & 3;
-  // address = 65536 * buffer + 256 * weight byte + 2 * slot: byte 0 from the
-  // lane constant (2 * slot), byte 1 the weight byte, byte 2 the buffer
-  // (0 from the selector's zero, 1 from the lane constant's byte 2)
-  uint32_t lc[4][4];
-  uint32_t selb[2][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t b = (i + r4) & 3;
-    selb[0][i] = 0u | ((4u + b) << 8) | (0x0Cu << 16) | (0x0Cu << 24);
-    selb[1][i] = 0u | ((4u + b) << 8) | (0x02u << 16) | (0x0Cu << 24);
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-      lc[d][i] = static_cast<uint32_t>(2 * lut_slot(16 * c + 4 * d + static_cast<int>(b))) |
-                 (1u << 16);
-  }
-
-  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t*>(w), (short)0, static_cast<int>(w_bytes), 0x00020000);
-  const __amdgpu_buffer_rsrc_t lres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(lut), (short)0, static_cast<int>(lut_bytes), 0x00020000);
-  const uint32_t row_bytes = static_cast<uint32_t>(ldw * 4);
-
-  auto load_unit = [&](int64_t u, uint4* wv) {
-    const bool ok = u <= u_last;
-    const int64_t rb = u / sc.S;
-    const int sl = static_cast<int>(u - rb * sc.S);
-    const int j_lo = (ok && u == u_begin) ? static_cast<int>(g_begin - u * JR) : 0;
-    const int j_hi = (ok && u == u_last) ? static_cast<int>(g_end - u * JR) : JR;
-    const uint32_t base = static_cast<uint32_t>(
-        (rb * R + wave * 8 + r) * (int64_t)row_bytes + (int64_t)sl * kSliceBytes + 16 * c);
-#pragma unroll
-    for (int j = 0; j < JR; ++j) {
-      const uint32_t off = (ok && j >= j_lo && j < j_hi)
-                               ? base + static_cast<uint32_t>(j * kV3RowsPerStep) * row_bytes
-                               : kNoLoad;
-      const auto v = __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, 0);
-      __builtin_memcpy(&wv[j], &v, 16);
-    }
-  };
-  // 64 KB table of unit u into LDS buffer `buf`: 4 loads of 16 bytes per lane
-  auto load_table = [&](int64_t u, int buf) {
-    const bool ok = u <= u_last;
-    const int sl = static_cast<int>(u - (u / sc.S) * sc.S);
-    const uint32_t soff = ok ? static_cast<uint32_t>(sl) * 65536u : kNoLoad;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int chunk = k * kV3Waves + wave;                       // 1 KB per wave
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          lres, (__attribute__((address_space(3))) void*)(tabs + buf * 65536 + chunk * 1024), 16,
-          static_cast<uint32_t>(chunk * 1024 + lane * 16), soff, 0, 0);
-    }
-  };
-
-  float acc[JR];
-#pragma unroll
-  for (int j = 0; j < JR; ++j) acc[j] = 0.f;
-
-  auto flush = [&](int64_t rb) {
-#pragma unroll
-    for (int j = 0; j < JR; ++j) acc[j] = sum8(acc[j]);
-    const int64_t g0 = rb * sc.S * JR;
-    const int w_first = owner(g0, sc.T, sc.G);
-    const int w_last = owner(g0 + (int64_t)sc.S * JR - 1, sc.T, sc.G);
-    const int n = w_last - w_first + 1;
-    if (n == 1) {
-      if (c == 0) {
-#pragma unroll
-        for (int j = 0; j < JR; ++j) {
-          const int64_t row = rb * R + j * kV3RowsPerStep + wave * 8 + r;
-          if (row < m) out[row] = s[row] * acc[j];
-        }
-      }
-    } else {
-      const int k = wg - w_first;
-      float* pb = partials + (rb * sc.kmax + k) * (int64_t)R;
-      if (c == 0) {
-#pragma unroll
-        for (int j = 0; j < JR; ++j)
-          __hip_atomic_store(pb + j * kV3RowsPerStep + wave * 8 + r, acc[j], __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (tid == 0) {
-        const unsigned prev = __hip_atomic_fetch_add(&counters[rb], 1u, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (prev == static_cast<unsigned>(n - 1)) ? 1 : 0;
-      }
-      __syncthreads();
-      if (s_last) {
-        const float* p0 = partials + rb * sc.kmax * (int64_t)R;
-        for (int rr = tid; rr < R; rr += kV3Threads) {
-          const int64_t row = rb * R + rr;
-          if (row < m) {
-            float sum = 0.f;
-            for (int k0 = 0; k0 < n; k0 += 8) {
-              float v[8];
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                v[e] = (k0 + e < n) ? __hip_atomic_load(p0 + (int64_t)(k0 + e) * R + rr,
-                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                    : 0.f;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) sum += v[e];
-            }
-            out[row] = s[row] * sum;
-          }
-        }
-        if (tid == 0)
-          __hip_atomic_store(&counters[rb], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < JR; ++j) acc[j] = 0.f;
-  };
-
-  uint4 wbuf[2][JR];
-  load_table(u_begin, 0);
-  load_unit(u_begin, wbuf[0]);
-
-  // One unit in buffer `buf`: wait for its table (issued one unit earlier,
-  // ahead of its weights), then request the next unit's table and weights,
-  // then look up.  Steps past the end still issue their (empty) loads so the
-  // unrolled loop's register flow never changes.
-  auto do_unit = [&](int64_t u, bool active, int buf, const uint4* cur, uint4* nxt) {
-    const int64_t rb = u / sc.S;
-    const int j_lo = (u == u_begin) ? static_cast<int>(g_begin - u * JR) : 0;
-    const int j_hi = (u == u_last) ? static_cast<int>(g_end - u * JR) : JR;
-    // outstanding here, oldest first: this table (4), this unit's weights (JR)
-    __builtin_amdgcn_s_waitcnt(0x0F70 | (JR & 15) | ((JR >> 4) << 14));
-    __syncthreads();                    // every wave's part of the table landed;
-                                        // the other buffer is no longer read
-    load_table(u + 1, buf ^ 1);
-    load_unit(u + 1, nxt);
-    if (active) {
-      const char* tb = reinterpret_cast<const char*>(tabs);
-#pragma unroll
-      for (int j = 0; j < JR; ++j) {
-        if (j >= j_lo && j < j_hi) {
-          const uint32_t wd[4] = {cur[j].x, cur[j].y, cur[j].z, cur[j].w};
-          float a = acc[j];
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-              const uint32_t ad = __builtin_amdgcn_perm(wd[d], lc[d][i], selb[buf][i]);
-              a = add_f16_lo(a, *reinterpret_cast<const uint16_t*>(tb + ad));
-            }
-          acc[j] = a;
-        }
-      }
-      if (u == u_last || (u + 1) / sc.S != rb) flush(rb);
-    }
-  };
-
-  for (int64_t u = u_begin; u <= u_last; u += 2) {
-    do_unit(u, true, 0, wbuf[0], wbuf[1]);
-    do_unit(u + 1, u + 1 <= u_last, 1, wbuf[1], wbuf[0]);
-  }
-}
-
 }  // namespace
 
+static int g_num_cus[64] = {0};
+
+int num_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (g_num_cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    g_num_cus[dev] = n;
+  }
+  return g_num_cus[dev];
+}
+
 size_t gemv_counter_bytes(int64_t m) {
-  // one arrival counter per row block (row blocks are >= 64 rows)
-  return ((size_t)((m + 63) / 64) * sizeof(unsigned) + 255) / 256 * 256;
+  // One 128-byte line per 16 rows: the one-token kernel keeps one counter
+  // per block of 16, 32 or 64 rows at the head of a line, this one a counter
+  // per row block (>= 512 rows) at the start of the region.  Both kernels put
+  // their partial sums after the same counter region and leave every counter
+  // at zero, so one workspace serves either.
+  return ((size_t)((m + 15) / 16) * 128 + 255) / 256 * 256;
 }
 
 GemvPlan plan_gemv(int64_t m, int64_t K, int64_t B) {
@@ -631,30 +356,6 @@ GemvPlan plan_gemv(int64_t m, int64_t K, int64_t B) {
                  sizeof(float) * (size_t)sc.rbs * sc.kmax * nt * (size_t)p.rows_per_wg;
   return p;
 }
-
-// Workspace of the batch-1 path: [arrival counters][partial sums][tables].
-size_t gemv1_lut_offset(int64_t m, int64_t K) {
-  const Sched sc = make_sched(m, K, kV3JR, num_cus(), kV3RowsPerStep);
-  size_t b = gemv_counter_bytes(m);
-  if (sc.kmax > 1) b += ((sizeof(float) * (size_t)sc.rbs * sc.kmax * kV3R) + 255) / 256 * 256;
-  return b;
-}
-
-size_t gemv1_workspace_bytes(int64_t m, int64_t K) {
-  return gemv1_lut_offset(m, K) + static_cast<size_t>(lut_bytes(1, K));
-}
-
-hipError_t launch_gemv1_lut(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
-                            const void* lut, float* out, void* ws, hipStream_t st) {
-  const Sched sc = make_sched(m, K, kV3JR, num_cus(), kV3RowsPerStep);
-  unsigned* counters = static_cast<unsigned*>(ws);
-  float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + gemv_counter_bytes(m));
-  hipLaunchKernelGGL(gemv1_lut_kernel, dim3(sc.G), dim3(kV3Threads), 0, st, w, m, ldw, s,
-                     static_cast<const uint16_t*>(lut), out, partials, counters, sc,
-                     static_cast<uint32_t>(m * ldw * 4), static_cast<uint32_t>(lut_bytes(1, K)));
-  return hipGetLastError();
-}
-
 
 size_t gemv_workspace_bytes(int64_t m, int64_t K, int64_t B) {
   size_t mx = 0;

@@ -1,0 +1,486 @@
+// One-token product of 1-bit weights with float lifted activations:
+//   out[i] = s[i] * sum_k sigma_ik * a_hat[k],  sigma = 2*bit - 1
+// (LiftQuant notes, 关键设计 4: after the activation transform the layer is a
+// product of 1-bit weights with floats, scaled per row by s).
+//
+// The weights stream from HBM once; each weight byte costs one table read and
+// one add, against tables of signed activation sums.  A table serves one
+// 1024-bit slice of the lifted dimension,
+//   E_p[v] = sum_{t<8} (2*bit_t(v) - 1) * a_hat[1024 sl + 8p + t]   (p < 128, v < 256),
+// and costs about as much to build as a few thousand rows of lookups, so it
+// has to serve many rows: the work is ordered slice-major.
+//
+// Tables are float16 (64 KB per slice), so that the two slices a workgroup's
+// range can straddle both stay in LDS and no wave ever waits for another.
+// Each table is built from the slice's activations scaled by a power of two
+// that puts the largest possible entry (8 max|a|) just below 2^14, and the
+// row sums are scaled back by the inverse power: the scaling is exact, and
+// each entry carries one float16 rounding (relative 2^-11) whatever the range
+// of the activations.  Lookups add the float16 entries in float32.
+//
+// Work split.  Granule = 16 rows x one slice (2 KB of weights).  The granules
+// are ordered (slice, row) and cut into one equal range per workgroup (one
+// workgroup per CU), so a workgroup covers a long run of rows of one or two
+// slices.  In each slice the 16 waves split the workgroup's granules into 16
+// contiguous runs; each wave streams its runs on its own with a ring of DEPTH
+// granules of loads in flight (lane (r, c) loads 16 bytes of rows r and r + 8
+// of the granule, 8 lanes per row).
+//
+// Reduction over slices.  Each granule leaves its 16 row sums of one slice in
+// the workspace (plain stores); a second kernel adds each row's S partial
+// sums in slice order (4 lanes per row, then a fixed tree), scales by s and
+// writes the row, so the result does not depend on timing.  Split-K with an
+// in-kernel last-arriver reduction would put the slowest wave's reductions on
+// the critical path; the kernel boundary costs less than that.
+#include <type_traits>
+
+#include "lut_common.h"
+
+namespace lq {
+namespace {
+
+#ifndef LQ_GEMV1_WAVES
+#define LQ_GEMV1_WAVES 16
+#endif
+#ifndef LQ_GEMV1_DEPTH
+#define LQ_GEMV1_DEPTH 3
+#endif
+constexpr int kWaves = LQ_GEMV1_WAVES;         // 16: four waves per SIMD
+constexpr int kThreads = 64 * kWaves;
+constexpr int kDepth = LQ_GEMV1_DEPTH;         // granules in flight per wave
+constexpr int kGranuleRows = 16;
+constexpr int kMaxGroups = 256;                // workgroups of one launch (at most)
+// A workgroup whose range crosses a slice boundary builds two tables and
+// runs two padded runs per wave: it gets this fraction less work.
+#ifndef LQ_GEMV1_STRADDLE
+#define LQ_GEMV1_STRADDLE 0.2
+#endif
+constexpr double kStraddleCost = LQ_GEMV1_STRADDLE;
+constexpr int kTableHalves = 32768;            // float16 entries per table
+
+// Slot of byte position p = 16c + 4d + b of a slice (c: 16-byte chunk, d:
+// dword, b: byte) in a float16 table, whose entry (slot, v) sits at byte
+// 256 v + 2 slot:  slot bits [0] = d & 1, [2:1] = b, [5:3] = c, [6] = d >> 1.
+// At lookup step i, lane (r, c) reads byte b = (i + r) & 3 of its dword d;
+// the 32 lanes of a half-wave (r < 4) then hit banks (slot >> 1) % 32 =
+// 4c + b: all different.  h_pos inverts h_slot.
+__host__ __device__ constexpr int h_slot(int p) {
+  return ((p >> 2) & 1) | ((p & 3) << 1) | (((p >> 4) & 7) << 3) | (((p >> 3) & 1) << 6);
+}
+__host__ __device__ constexpr int h_pos(int sl) {
+  return 16 * ((sl >> 3) & 7) + 4 * ((sl & 1) | (((sl >> 6) & 1) << 1)) + ((sl >> 1) & 3);
+}
+
+struct Sched1 {
+  int64_t NG;   // 16-row granules per slice
+  int64_t T;    // granules in all: S * NG
+  int S;        // 1024-bit slices
+  int G;        // workgroups
+  int64_t start[kMaxGroups + 1];   // workgroup w: granules [start[w], start[w + 1])
+};
+
+// v, available only once `dep` is: ties a later memory operation to the wait
+// for the load that produced `dep`.
+__device__ __forceinline__ uint32_t after(uint32_t v, uint32_t dep) {
+  asm volatile("; after %1" : "+v"(v) : "v"(dep));
+  return v;
+}
+
+// acc + the float16 in the low half of h, in float32 (one v_fma_mix_f32).
+__device__ __forceinline__ float add_h(float acc, uint32_t h) {
+  float r;
+  asm("v_fma_mix_f32 %0, %1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(acc));
+  return r;
+}
+
+// Power of two 2^(11 - e) with max|x| = f * 2^e, f in [0.5, 1): entries of
+// the scaled table stay below 8 * 2^e * 2^(11 - e) = 2^14.
+// e_up = e - 11 is the exponent of the inverse.
+__device__ __forceinline__ float table_scale(float xmax, int& e_up) {
+  if (!(xmax > 0.f)) {
+    e_up = 0;
+    return 1.f;
+  }
+  int e;
+  (void)frexpf(xmax, &e);
+  e_up = e - 11;
+  return ldexpf(1.f, 11 - e);
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// Two float32 values as two float16 (round to nearest even) in one word.
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+  const float2_t f = {lo, hi};
+  const half2_t h = __builtin_convertvector(f, half2_t);   // v_cvt_pk_f16_f32
+  uint32_t u;
+  __builtin_memcpy(&u, &h, 4);
+  return u;
+}
+
+// Float16 table of one slice, built by the WAVES waves.  Flipping every bit
+// of a weight byte flips every sign, so E[255 - v] = -E[v]: wave w computes
+// the entries of v in [VB w, VB w + VB), VB = 128 / WAVES (low bits of v in
+// Gray-code order, one add per entry), and writes them and their negations
+// (sign bits flipped: exact) for slots 2 lane and 2 lane + 1, one packed
+// 32-bit LDS store per v.  x0, x1: the 8 scaled activations of the byte
+// positions of the two slots.
+template <int WAVES>
+__device__ __forceinline__ void build_table16(uint16_t* __restrict__ tab, const float (&x0)[8],
+                                              const float (&x1)[8], int wave, int lane) {
+  constexpr int VB = 128 / WAVES;
+  constexpr int LB = VB == 16 ? 4 : VB == 8 ? 3 : 2;     // Gray-coded low bits
+  float v0 = -x0[7], v1 = -x1[7];                          // bit 7 of v is 0
+#pragma unroll
+  for (int t = 0; t < LB; ++t) {
+    v0 -= x0[t];
+    v1 -= x1[t];
+  }
+#pragma unroll
+  for (int t = LB; t < 7; ++t) {
+    const bool on = (wave >> (t - LB)) & 1;
+    v0 += on ? x0[t] : -x0[t];
+    v1 += on ? x1[t] : -x1[t];
+  }
+  uint32_t* lo = reinterpret_cast<uint32_t*>(tab) + (VB * wave) * 64 + lane;
+  uint32_t* hi = reinterpret_cast<uint32_t*>(tab) + (255 - VB * wave) * 64 + lane;
+  auto put = [&](int i) {
+    const uint32_t h = pack_h2(v0, v1);
+    lo[gray(i) * 64] = h;
+    hi[-gray(i) * 64] = h ^ 0x80008000u;
+  };
+  put(0);
+#pragma unroll
+  for (int i = 1; i < VB; ++i) {
+    const int t = ctz6(i);
+    const bool up = (gray(i) >> t) & 1;
+    v0 = up ? v0 + 2.f * x0[t] : v0 - 2.f * x0[t];
+    v1 = up ? v1 + 2.f * x1[t] : v1 - 2.f * x1[t];
+    put(i);
+  }
+}
+
+template <bool SPLIT>
+__global__ void __launch_bounds__(kThreads, 1) gemv1_kernel(
+    const uint32_t* __restrict__ w, int64_t m, int64_t K, int64_t ldw,
+    const float* __restrict__ s, const float* __restrict__ ah, float* __restrict__ out,
+    float* __restrict__ partials, Sched1 sc, uint32_t w_bytes, uint32_t a_bytes) {
+  __shared__ __attribute__((aligned(16))) uint16_t tabs[2 * kTableHalves];   // 128 KB
+  static_assert(kWaves >= 8 && (kWaves & (kWaves - 1)) == 0 && kWaves <= 32, "8..32 waves");
+  constexpr int D = kDepth;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t t_begin = sc.start[blockIdx.x];
+  const int64_t t_end = sc.start[blockIdx.x + 1];
+  if (t_begin >= t_end) return;
+  const int sl_first = static_cast<int>(t_begin / sc.NG);
+  const int sl_last = static_cast<int>((t_end - 1) / sc.NG);
+  const int NG = static_cast<int>(sc.NG);       // < 2^22: m * ldw * 4 <= 2^30, ldw >= 4
+
+  const int r = lane >> 3;                      // rows r and r + 8 of the granule
+  const int c = lane & 7;                       // 16-byte chunk of the 128-byte slice row
+  // Address of entry (slot, v) of table t for byte b of dword d of the
+  // lane's chunk: 2 slot = (16c + 4b) + (2 (d & 1) + 128 (d >> 1)).  One
+  // v_perm_b32 builds 65536 t + 256 v + 16c + 4b from the weight dword (byte
+  // 1: the weight byte) and a lane constant (byte 0: 16c + 4b, byte 2: t);
+  // the part that depends on d only goes in the LDS read's offset field.
+  uint32_t lc[2][4], sel[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t b = (i + (r & 3)) & 3;
+    sel[i] = 0u | ((4u + b) << 8) | (0x02u << 16) | (0x0Cu << 24);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) lc[t][i] = (16u * c + 4u * b) | (static_cast<uint32_t>(t) << 16);
+  }
+  constexpr int kDwordOff[4] = {0, 2, 128, 130};
+
+  // Weight loads: per-lane offsets (rows r and r + 8, chunk c) plus a scalar
+  // granule offset.  Lanes past the row's last weight byte read bytes that
+  // pair with zero activations (their entries are 0); rows past m fall past
+  // the end of `w` (w_bytes = m * row_bytes), where the buffer's range check
+  // returns zeros, as it does for the scalar kNoLoad.  Offsets stay below
+  // 2^31 + 2^25 (row_bytes <= 2^21), so nothing wraps.
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(w), (short)0, static_cast<int>(w_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(ah), (short)0, static_cast<int>(a_bytes), 0x00020000);
+  const uint32_t row_bytes = static_cast<uint32_t>(ldw * 4);
+  const uint32_t granule_bytes = kGranuleRows * row_bytes;
+  const uint32_t lane_off0 = static_cast<uint32_t>(r) * row_bytes + 16 * c;
+  const uint32_t lane_off1 = lane_off0 + 8 * row_bytes;
+
+  // This workgroup's granules of slice sl: [lo, hi) within the slice; this
+  // wave's run of them: [run_a, run_b).
+  auto lo_of = [&](int sl) -> int {
+    const int64_t v = t_begin - (int64_t)sl * sc.NG;
+    return v > 0 ? static_cast<int>(v) : 0;
+  };
+  auto hi_of = [&](int sl) -> int {
+    const int64_t v = t_end - (int64_t)sl * sc.NG;
+    return static_cast<int>(v < sc.NG ? v : sc.NG);
+  };
+  auto run_a = [&](int sl) -> int {
+    const int lo = lo_of(sl);
+    return lo + (wave * (hi_of(sl) - lo)) / kWaves;
+  };
+  auto run_b = [&](int sl) -> int {
+    const int lo = lo_of(sl);
+    return lo + ((wave + 1) * (hi_of(sl) - lo)) / kWaves;
+  };
+
+  // Load cursor (all scalar).  Each slice's run is processed in rounds of D
+  // ring slots, the last round padded with empty slots, so every slice
+  // starts at slot 0; the cursor runs one round ahead of the granules being
+  // processed and so only changes slice between rounds.
+  int ld_sl = sl_first - 1, ld_k = 0, ld_n = 0, ld_slots = 0;
+  uint32_t ld_off = 0;                          // offset of the next granule of the run
+  auto ld_next_slice = [&]() {
+    do {
+      ++ld_sl;
+      ld_k = 0;
+      if (ld_sl <= sl_last) {
+        const int a = run_a(ld_sl);
+        ld_n = run_b(ld_sl) - a;
+        ld_slots = (ld_n + D - 1) / D * D;
+        ld_off = static_cast<uint32_t>(a) * granule_bytes +
+                 static_cast<uint32_t>(ld_sl) * kSliceBytes;
+      } else {
+        ld_n = 0;
+        ld_slots = 1 << 30;
+      }
+    } while (ld_slots == 0);
+  };
+  auto issue = [&](uint4 (&dst)[2]) {
+    const uint32_t so = ld_k < ld_n ? ld_off : kNoLoad;
+    const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(wres, lane_off0, so, 0);
+    const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(wres, lane_off1, so, 0);
+    ld_off += granule_bytes;
+    ++ld_k;
+    __builtin_memcpy(&dst[0], &v0, 16);
+    __builtin_memcpy(&dst[1], &v1, 16);
+  };
+
+  // Tables of slices sp and sp + 1 (the second only if the range reaches
+  // it).  Every wave builds part of each table for all 128 slots (lane l:
+  // slots 2l and 2l + 1), so it loads the activations of all the slice's byte
+  // positions, and takes their largest magnitude (the table's scale) in the
+  // wave.  These loads are issued before any weight load of the workgroup
+  // (the first barrier), so the weights queue behind them; with `first` each
+  // wave then issues two granules of weights, which stream in while the
+  // tables are built, and the rest of its ring after (issuing all of it at
+  // once would stall on the full memory queue).
+  uint4 wb[D][2];
+  float scale_up[2];
+  auto tables = [&](int sp, bool first) {
+    const int nt = sp + 1 <= sl_last ? 2 : 1;
+    float4 xa[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (t < nt) {
+        load_x(ares, K, 0, sp + t, h_pos(2 * lane), xa[t][0], xa[t][1]);
+        load_x(ares, K, 0, sp + t, h_pos(2 * lane + 1), xa[t][2], xa[t][3]);
+      }
+    }
+    __syncthreads();                            // activations requested before any weight;
+                                                // nobody reads the old tables any more
+    if (first) {
+      ld_next_slice();
+      issue(wb[0]);
+      issue(wb[1]);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (t < nt) {
+        float mx = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          mx = fmaxf(mx, fmaxf(fmaxf(fabsf(xa[t][k].x), fabsf(xa[t][k].y)),
+                               fmaxf(fabsf(xa[t][k].z), fabsf(xa[t][k].w))));
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        int e_up;
+        const float sd = table_scale(mx, e_up);
+        scale_up[t] = ldexpf(1.f, e_up);        // exact inverse of sd
+        const float y0[8] = {xa[t][0].x * sd, xa[t][0].y * sd, xa[t][0].z * sd, xa[t][0].w * sd,
+                             xa[t][1].x * sd, xa[t][1].y * sd, xa[t][1].z * sd, xa[t][1].w * sd};
+        const float y1[8] = {xa[t][2].x * sd, xa[t][2].y * sd, xa[t][2].z * sd, xa[t][2].w * sd,
+                             xa[t][3].x * sd, xa[t][3].y * sd, xa[t][3].z * sd, xa[t][3].w * sd};
+        build_table16<kWaves>(tabs + t * kTableHalves, y0, y1, wave, lane);
+      }
+    }
+    __syncthreads();
+    if (first) {
+#pragma unroll
+      for (int e = 2; e < D; ++e) issue(wb[e]);
+    }
+  };
+  tables(sl_first, true);
+
+  const char* tb = reinterpret_cast<const char*>(tabs);
+  // Sum of the table-TI entries of one row's 16 weight bytes held by a lane.
+  auto lookup_row = [&]<int TI>(const uint32_t (&wd)[4]) -> float {
+    float a[4];
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      a[d] = add_h(0.f, *reinterpret_cast<const uint16_t*>(
+                            tb + __builtin_amdgcn_perm(wd[d], lc[TI][0], sel[0]) + kDwordOff[d]));
+#pragma unroll
+    for (int i = 1; i < 4; ++i)
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        a[d] = add_h(a[d], *reinterpret_cast<const uint16_t*>(
+                               tb + __builtin_amdgcn_perm(wd[d], lc[TI][i], sel[i]) +
+                               kDwordOff[d]));
+    return (a[0] + a[1]) + (a[2] + a[3]);
+  };
+  int rnd = 0;                                  // rounds processed so far
+  auto process_run = [&](auto tsel, int sl) {
+    constexpr int TI = decltype(tsel)::value;
+    const int a = run_a(sl);
+    const int n = run_b(sl) - a;
+    const float up = scale_up[TI];
+    float* pout = SPLIT ? partials + ((int64_t)a * sc.S + sl) * kGranuleRows
+                        : out + (int64_t)kGranuleRows * a;
+    const float* ps = s + (int64_t)kGranuleRows * a;
+    const int64_t pstep = SPLIT ? (int64_t)sc.S * kGranuleRows : kGranuleRows;
+    for (int k0 = 0; k0 < n; k0 += D, ++rnd) {
+      if (ld_k >= ld_slots) ld_next_slice();    // this round's loads go to the next slice
+      uint32_t dep0 = 0;                        // a word of the round's first granule
+#pragma unroll
+      for (int e = 0; e < D; ++e) {
+        if (k0 + e < n) {                       // always true for e = 0
+          const uint32_t wd0[4] = {wb[e][0].x, wb[e][0].y, wb[e][0].z, wb[e][0].w};
+          const uint32_t wd1[4] = {wb[e][1].x, wb[e][1].y, wb[e][1].z, wb[e][1].w};
+          if (e == 0) dep0 = wd0[0];
+          // one row's lookups at a time keeps the loaded entries of only 16
+          // lookups live
+          const float v0 = sum8(lookup_row.template operator()<TI>(wd0)) * up;
+          __builtin_amdgcn_sched_barrier(0);
+          const float v1 = sum8(lookup_row.template operator()<TI>(wd1)) * up;
+          // lanes c = 0 and 1 write rows r and r + 8
+          const int rr = r + 8 * c;
+          const float v = c == 0 ? v0 : v1;
+          if constexpr (SPLIT) {
+            if (c < 2) pout[rr] = v;
+          } else {
+            const int64_t row = (int64_t)kGranuleRows * (a + k0 + e) + rr;
+            if (c < 2 && row < m) pout[rr] = ps[rr] * v;
+            ps += pstep;
+          }
+          pout += pstep;
+        }
+        issue(wb[e]);
+      }
+    }
+  };
+
+  for (int sl = sl_first; sl <= sl_last; ++sl) {   // the same slices in every wave
+    const int rel = sl - sl_first;
+    if (rel >= 2 && (rel & 1) == 0) tables(sl, false);   // only when the range spans > 2 slices
+    if ((rel & 1) == 0)
+      process_run(std::integral_constant<int, 0>{}, sl);
+    else
+      process_run(std::integral_constant<int, 1>{}, sl);
+  }
+}
+
+// out[i] = s[i] * (sum over slices q of partials[i / 16][q][i % 16]), added in
+// a fixed order: a wave takes one 16-row granule, lane (part, row) = (l / 16,
+// l % 16) adds slices part, part + 4, ... in order (all its loads issued
+// before the first add: one round trip while S <= 128), then the 4 parts of
+// a row combine by a fixed tree.
+__global__ void __launch_bounds__(256) gemv1_reduce_kernel(const float* __restrict__ partials,
+                                                           const float* __restrict__ s,
+                                                           float* __restrict__ out, int64_t m,
+                                                           int S) {
+  const int lane = threadIdx.x & 63;
+  const int64_t g = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+  const int rr = lane & 15;
+  const int part = lane >> 4;
+  const int64_t row = g * kGranuleRows + rr;
+  const float* p = partials + (g * S) * kGranuleRows + rr;
+  float sum = 0.f;
+  if (row < m) {
+    for (int q0 = part; q0 < S; q0 += 4 * 32) {
+      float v[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int q = q0 + 4 * u;
+        v[u] = q < S ? p[(int64_t)q * kGranuleRows] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 32; ++u) sum += v[u];
+    }
+  }
+  sum += __shfl_xor(sum, 16);
+  sum += __shfl_xor(sum, 32);
+  if (row < m && part == 0) out[row] = s[row] * sum;
+}
+
+// Ranges of the workgroups over the (slice, granule) order.  A range that
+// crosses a slice boundary pays for a second table and a second run per
+// wave, about kStraddleCost of a share: the granules are laid on a line with
+// a gap of c = kStraddleCost * share after each slice, the line is cut into
+// G equal pieces, and each piece takes the granules it covers (a piece that
+// contains a gap gets c fewer).  Cut points inside a gap go to the slice end.
+Sched1 make_sched1(int64_t m, int64_t K) {
+  Sched1 sc{};
+  sc.S = static_cast<int>((K + kSliceBits - 1) / kSliceBits);
+  sc.NG = (m + kGranuleRows - 1) / kGranuleRows;
+  sc.T = sc.NG * sc.S;
+  const int64_t gmax = (sc.T + kWaves - 1) / kWaves;
+  int cus = num_cus();
+  if (cus > kMaxGroups) cus = kMaxGroups;
+  sc.G = static_cast<int>(gmax < cus ? gmax : cus);
+  const double share = (double)sc.T / sc.G;
+  const double c = share < (double)sc.NG ? kStraddleCost * share : 0.0;
+  const double span = (double)sc.NG + c;                 // a slice and its gap
+  const double V = (double)sc.T + (sc.S - 1) * c;
+  for (int w = 0; w < sc.G; ++w) {
+    const double v = V * w / sc.G;
+    int64_t sl = (int64_t)(v / span);
+    if (sl >= sc.S) sl = sc.S - 1;
+    double off = v - sl * span;
+    if (off > (double)sc.NG) off = (double)sc.NG;
+    int64_t t = sl * sc.NG + (int64_t)(off + 1e-9);
+    if (t > sc.T) t = sc.T;
+    if (w > 0 && t < sc.start[w - 1]) t = sc.start[w - 1];
+    sc.start[w] = t;
+  }
+  sc.start[sc.G] = sc.T;
+  return sc;
+}
+
+}  // namespace
+
+size_t gemv1_workspace_bytes(int64_t m, int64_t K) {
+  const Sched1 sc = make_sched1(m, K);
+  if (sc.S == 1) return 0;
+  // partial sums after the counter region of the several-token kernel, which
+  // must stay zero
+  return gemv_counter_bytes(m) + sizeof(float) * kGranuleRows * (size_t)sc.NG * sc.S;
+}
+
+hipError_t launch_gemv1(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
+                        const float* a_lift, float* out, void* ws, hipStream_t st) {
+  const Sched1 sc = make_sched1(m, K);
+  const uint32_t w_bytes = static_cast<uint32_t>(m * ldw * 4);
+  const uint32_t a_bytes = static_cast<uint32_t>(K * 4);
+  if (sc.S == 1) {
+    hipLaunchKernelGGL(gemv1_kernel<false>, dim3(sc.G), dim3(kThreads), 0, st, w, m, K, ldw, s,
+                       a_lift, out, nullptr, sc, w_bytes, a_bytes);
+  } else {
+    float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + gemv_counter_bytes(m));
+    hipLaunchKernelGGL(gemv1_kernel<true>, dim3(sc.G), dim3(kThreads), 0, st, w, m, K, ldw, s,
+                       a_lift, out, partials, sc, w_bytes, a_bytes);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gemv1_reduce_kernel, dim3(static_cast<unsigned>((sc.NG + 3) / 4)),
+                       dim3(256), 0, st, partials, s, out, m, sc.S);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace lq

@@ -152,14 +152,10 @@ lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw, c
       return fail(LQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
     if (!aligned(workspace, 256)) return fail(LQ_ERR_ALIGN, "workspace must be 256-byte aligned");
   }
-  if (B == 1) {
-    // one token: float16 activation-sum tables, then the table-driven kernel
-    void* lut = static_cast<char*>(workspace) + lq::gemv1_lut_offset(m, K);
-    hipError_t e = lq::launch_build_lut(a_lift, 1, K, lut, as_stream(stream));
-    if (e == hipSuccess)
-      e = lq::launch_gemv1_lut(w_packed, m, K, ldw, s, lut, out, workspace, as_stream(stream));
-    return hip_status(e, "lq_gemv launch");
-  }
+  if (B == 1)
+    return hip_status(lq::launch_gemv1(w_packed, m, K, ldw, s, a_lift, out, workspace,
+                                       as_stream(stream)),
+                      "lq_gemv launch");
   // Tokens go through in groups of at most 4; each group rereads the weights.
   for (int64_t t0 = 0; t0 < B; t0 += 4) {
     const int64_t bt = (B - t0) < 4 ? (B - t0) : 4;

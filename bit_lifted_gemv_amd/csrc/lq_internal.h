@@ -68,24 +68,6 @@ __device__ __forceinline__ void store_from_float<LQ_BF16>(void* p, int64_t i, fl
   static_cast<uint16_t*>(p)[i] = float_to_bf16_bits_rne(v);
 }
 
-// ---------------------------------------------------------------- float16 tables
-// Slot of byte position p = 16c + 4d + b of a 1024-bit slice (c: 16-byte
-// chunk, d: dword, b: byte) in the float16 activation-sum tables:
-//   slot bits [0] = d & 1, [2:1] = b, [5:3] = c, [6] = d >> 1.
-// For any fixed (d, b-rotation), the 32 lanes of a half-wave that read
-// chunks c = 0..7 at four different bytes b hit banks (slot >> 1) % 32 =
-// 4c + b: all different.
-__host__ __device__ constexpr int lut_slot(int p) {
-  return ((p >> 2) & 1) | ((p & 3) << 1) | (((p >> 4) & 7) << 3) | (((p >> 3) & 1) << 6);
-}
-__host__ __device__ constexpr int lut_pos(int sl) {
-  return 16 * ((sl >> 3) & 7) + 4 * ((sl & 1) | (((sl >> 6) & 1) << 1)) + ((sl >> 1) & 3);
-}
-constexpr int64_t kLutTableBytes = 256 * 128 * 2;    // one slice of one token
-__host__ __device__ constexpr int64_t lut_bytes(int64_t B, int64_t K) {
-  return B * ((K + 1023) / 1024) * kLutTableBytes;
-}
-
 // ---------------------------------------------------------------- launchers
 hipError_t launch_pack_signs(const int8_t* signs, int64_t rows, int64_t K, int64_t lds,
                              uint32_t* packed, int64_t ldw, hipStream_t st);
@@ -96,6 +78,9 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t st);
 hipError_t launch_lift(const void* a, lq_dtype a_dt, int64_t B, int64_t n, const void* t_inv,
                        lq_dtype t_dt, const float* M, int d, int D, void* out, lq_dtype out_dt,
                        hipStream_t st);
+
+// Compute units of the current device (cached per device).
+int num_cus();
 
 // GEMV plan: how the rows and the lifted dimension are split over workgroups.
 struct GemvPlan {
@@ -114,13 +99,10 @@ hipError_t launch_gemv(const GemvPlan& plan, const uint32_t* w, int64_t m, int64
                        int64_t ldw, const float* s, const float* a_lift, int64_t B, float* out,
                        void* ws, hipStream_t st);
 
-hipError_t launch_build_lut(const float* a_lift, int64_t B, int64_t K, void* lut,
-                            hipStream_t st);
-// Batch-1 GEMV on float16 tables (lq_gemv with B == 1).
+// One-token GEMV (lq_gemv with B == 1).
 size_t gemv1_workspace_bytes(int64_t m, int64_t K);
-size_t gemv1_lut_offset(int64_t m, int64_t K);
-hipError_t launch_gemv1_lut(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
-                            const void* lut, float* out, void* ws, hipStream_t st);
+hipError_t launch_gemv1(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
+                        const float* a_lift, float* out, void* ws, hipStream_t st);
 
 hipError_t launch_gemm(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
                        const void* a_lift, lq_dtype dt, int64_t B, float* out, hipStream_t st);

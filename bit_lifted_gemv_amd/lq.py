@@ -146,9 +146,11 @@ def lift(a: torch.Tensor, t_inv: torch.Tensor, M: torch.Tensor, d: int, D: int,
 _WS = {}
 
 
-def workspace(nbytes: int, device: torch.device) -> torch.Tensor:
-    """A zeroed workspace of at least nbytes, cached per device (grown on demand)."""
-    key = (device.type, device.index)
+def workspace(nbytes: int, device: torch.device, m: int = 0) -> torch.Tensor:
+    """A zeroed GEMV workspace of at least nbytes for row count m, cached per
+    (device, m) and grown on demand: the library keeps the arrival counters at
+    its head zero between calls with the same m, not across row counts."""
+    key = (device.type, device.index, m)
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
@@ -172,7 +174,7 @@ def gemv(w_packed: torch.Tensor, s: torch.Tensor, a_lift: torch.Tensor, K: Optio
     if out is None:
         out = torch.empty((B, m), dtype=torch.float32, device=a_lift.device)
     nws = gemv_workspace_size(m, K, B)
-    ws = workspace(nws, a_lift.device) if nws else None
+    ws = workspace(nws, a_lift.device, m) if nws else None
     check(lib().lq_gemv(_ptr(w_packed), m, K, ldw, _ptr(s), _ptr(a_lift), B, _ptr(out), _ptr(ws),
                         nws, _stream(stream)))
     return out

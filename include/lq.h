@@ -109,8 +109,11 @@ lq_status lq_gemv_workspace_size(int64_t m, int64_t K, int64_t B, size_t* bytes)
 
 /*
  * lq_workspace_clear -- zero `bytes` bytes of a workspace on `stream` with a
- * fill kernel.  A new workspace must be cleared once before its first use;
- * every completed lq_gemv call leaves it cleared again.
+ * fill kernel.  A workspace must be cleared before its first use with a given
+ * row count m: its head holds arrival counters that must read zero, and every
+ * completed lq_gemv call with that m (any K, any B) leaves them zero again.
+ * A call with another m may find partial sums of an earlier call where its
+ * counters go: clear the workspace first, or keep one workspace per m.
  */
 lq_status lq_workspace_clear(void* workspace, size_t bytes, void* stream);
 
@@ -131,10 +134,13 @@ lq_status lq_workspace_clear(void* workspace, size_t bytes, void* stream);
  * workspace: device buffer of >= lq_gemv_workspace_size bytes, cleared once
  *           (lq_workspace_clear); may be NULL when that size is 0.
  * Requires 1 <= B <= 16, m >= 1, K >= 1, m*ldw*4 <= 2^30 bytes (split
- * larger matrices by rows over several calls) and K <= 2^24.  Accumulation is
- * float32; the result does not depend on timing (no float atomics).  With
- * B == 1 the activation sums are rounded to float16 before the float32
- * accumulation (relative output error ~3e-4); with B >= 2 they stay float32.
+ * larger matrices by rows over several calls) and K <= 2^24.  Accumulation
+ * is float32 and the result does not depend on timing (partial sums over the
+ * lifted dimension are added in a fixed order, no float atomics).  With
+ * B >= 2 the activation-sum tables are float32; with B == 1 they are float16,
+ * each slice's activations scaled by an exact power of two first, so every
+ * table entry carries one float16 rounding (relative 2^-11) whatever the
+ * range of a_lift: a relative output error of about 3e-4.
  */
 lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw,
                   const float* s, const float* a_lift, int64_t B, float* out,

@@ -21,11 +21,14 @@ from oracle import lq_oracle as O
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
+# With B >= 2 the GEMV adds float32 activation sums in float32 (about K/8 + 8
+# roundings per output on top of the float32 lifted operand): 1e-4 bounds it
+# with a wide margin at every K here.
 TOL_F32 = 1e-4
-# One token: the activation sums (8 terms each) are rounded to float16 (half
-# an ulp = 2^-11 relative) and then added in float32.  Independent rounding
-# errors give a relative output error of about 2^-11/sqrt(3) ~ 3e-4 in both
-# the largest error and the largest output; 1e-3 keeps a 3x margin.
+# With B == 1 each activation sum (8 terms) is rounded once to float16 after
+# an exact power-of-two scaling: relative error <= 2^-11 per table entry,
+# independent across the K/8 entries of a row, so the output error is about
+# 2^-11/sqrt(3) ~ 3e-4 of the output scale; 1e-3 keeps a 3x margin.
 TOL_LUT16 = 1e-3
 
 
@@ -101,6 +104,9 @@ def test_lift_16bit_outputs(dev, odt):
 GEMV_CASES = [  # (m, K, B): ragged rows, slices and token groups
     (1, 4, 1), (63, 512, 1), (65, 516, 1), (200, 1544, 2), (129, 3072, 3), (300, 2048, 4),
     (77, 1000, 5), (1000, 4100, 16), (4096, 10240, 1), (520, 9216, 7),
+    # one token: a single slice (no split), a 4-position last slice, a ragged
+    # 8-row granule, and more slices than workgroups (ranges over > 2 slices)
+    (1000, 1024, 1), (37, 1028, 1), (8193, 2048, 1), (64, 300000, 1),
 ]
 
 
@@ -131,6 +137,22 @@ def test_gemv_deterministic(dev):
     assert torch.equal(o1, o2)
 
 
+def test_gemv_token_counts_share_a_workspace(dev):
+    """Calls with one m and different B (different kernels and splits) run on
+    one workspace: each leaves the arrival counters zero for the next."""
+    _banner("gemv B = 1, 4, 1, 2, 1 on one workspace")
+    rng = np.random.default_rng(5)
+    m, K = 2050, 12288
+    packed = synth.random_sign_words(rng, m, K)
+    w = torch.from_numpy(packed.view(np.int32)).to(dev)
+    s = rng.uniform(0.01, 0.03, m).astype(np.float32)
+    sd = torch.from_numpy(s).to(dev)
+    for B in (1, 4, 1, 2, 1):
+        al = rng.standard_normal((B, K)).astype(np.float32)
+        got = lq.gemv(w, sd, torch.from_numpy(al).to(dev), K).cpu().numpy()
+        assert O.rel_err_colmax(got, O.lifted_product(packed, K, al, s)) <= (TOL_LUT16 if B == 1 else TOL_F32), B
+
+
 def test_gemv_all_ones_closed_form(dev):
     """All signs +1 (and all -1): out = +-s * sum_k a_lift[k]."""
     m, K = 130, 2560
@@ -142,6 +164,32 @@ def test_gemv_all_ones_closed_form(dev):
                       torch.from_numpy(s).to(dev), torch.from_numpy(al).to(dev), K).cpu().numpy()
         want = sign * s[None, :] * al.astype(np.float64).sum(axis=1)[:, None]
         assert O.rel_err_colmax(got, want) <= TOL_F32
+
+
+def test_gemv_one_token_scaling_is_exact(dev):
+    """One token: the tables are built from activations scaled by a power of
+    two chosen from their range, so scaling a_lift by 2^k scales every output
+    by exactly 2^k (no overflow, no loss for tiny or huge activations), and
+    the all-ones closed form holds."""
+    _banner("gemv B=1 power-of-two scaling")
+    rng = np.random.default_rng(9)
+    m, K = 700, 5120
+    packed = synth.random_sign_words(rng, m, K)
+    w = torch.from_numpy(packed.view(np.int32)).to(dev)
+    s = rng.uniform(0.01, 0.03, m).astype(np.float32)
+    sd = torch.from_numpy(s).to(dev)
+    al = rng.standard_normal((1, K)).astype(np.float32)
+    base = lq.gemv(w, sd, torch.from_numpy(al).to(dev), K).cpu().numpy()
+    assert O.rel_err_colmax(base, O.lifted_product(packed, K, al, s)) <= TOL_LUT16
+    for k in (-100, 100):
+        got = lq.gemv(w, sd, torch.from_numpy(np.ldexp(al, k)).to(dev), K).cpu().numpy()
+        assert np.array_equal(got, np.ldexp(base, k)), k
+    for fill, sign in ((0xFFFFFFFF, 1.0), (0, -1.0)):
+        ones = np.full((m, K // 32), fill, dtype=np.uint32)
+        got = lq.gemv(torch.from_numpy(ones.view(np.int32)).to(dev), sd,
+                      torch.from_numpy(al).to(dev), K).cpu().numpy()
+        want = sign * s[None, :] * al.astype(np.float64).sum(axis=1)[:, None]
+        assert O.rel_err_colmax(got, want) <= TOL_LUT16
 
 
 # ----------------------------------------------------------------- GEMM
