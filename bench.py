@@ -8,10 +8,12 @@ rotate over enough copies (> 2x the 256 MB Infinity Cache) that every step
 reads its weights from HBM.
 
 Printed: one JSON line with the whole-step algorithmic GB/s (`value`), the
-dominant kernel's roofline (GEMV: algorithmic bytes per launch / its average
-duration from HIP events on its stream), the batch-512 MFMA GEMM in TFLOP/s,
-per-workload GEMV figures, and the float64 oracle timed on the host cores over
-a bounded sample of the same workload.
+dominant kernel's roofline (the one-token GEMV: algorithmic bytes per call /
+the call's average duration from HIP events on its stream; the call is the
+weight-streaming kernel plus the small kernel that adds the per-slice partial
+sums, so the figure is conservative for the streaming kernel alone), the
+batch-512 MFMA GEMM in TFLOP/s, per-workload GEMV figures, and the float64
+oracle timed on the host cores over a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10]
 """
@@ -130,56 +132,91 @@ def run_gpu(args):
     al = [torch.empty((1, L.K), dtype=torch.float32, device=dev) for L in layers]
     outs = [torch.empty((1, L.m), dtype=torch.float32, device=dev) for L in layers]
 
-    ev = {}
-
-    def step(i, record=False):
+    def step(i):
         for j, (rot, L) in enumerate(zip(rots, layers)):
             c = rot[i]
             lq.lift(rot.a, c.t_inv, c.M, L.d, L.D, out=al[j])
-            if record:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(st)
             lq.gemv(c.w, c.s, al[j], L.K, out=outs[j])
-            if record:
-                e1.record(st)
-                ev.setdefault(j, []).append((e0, e1))
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    # One HIP graph per weight copy, each one whole step, so that the timed
+    # loop measures the GPU, not the host's launch rate.  Every graph's replay
+    # is checked bit for bit against the eager step on the same copy.
+    R = rots[0].R
+    graphs = capture_graphs(torch, [lambda k=k: step(k) for k in range(R)])
+    for k in range(R):
+        step(k)
+        torch.cuda.synchronize()
+        want = [o.clone() for o in outs]
+        for o in outs:
+            o.fill_(float("nan"))
+        graphs[k].replay()
+        torch.cuda.synchronize()
+        for o, w in zip(outs, want):
+            if not torch.equal(o, w):
+                raise RuntimeError(f"graph replay {k} differs from the eager step")
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, record=True)
+        graphs[(args.warmup + i) % R].replay()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
     step_bytes = sum(layer_bytes(L.m, L.n, L.d, L.D, 1) for L in layers)
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
-    # dominant kernel: GEMV; per-launch durations from the event pairs
+    # dominant kernel: the one-token GEMV call; per-call duration from HIP
+    # events around replays of a graph of back-to-back calls over the copies
     per = {}
-    for j, L in enumerate(layers):
-        d_ms = [a.elapsed_time(b) for a, b in ev[j]]
-        per[j] = float(np.mean(d_ms))
+    for j, (rot, L) in enumerate(zip(rots, layers)):
+        g = capture_graphs(torch, [lambda: [lq.gemv(rot[k].w, rot[k].s, al[j], L.K, out=outs[j])
+                                            for k in range(R)]])[0]
+        n_rep = max(3, min(args.steps, 20))
+        per[j] = time_launches(torch, lambda i: g.replay(), n_rep, st) / R
     g_bytes = [gemv_bytes(L.m, L.K, 1) for L in layers]
     gemv_ms = sum(per.values()) / len(per)
     gemv_bytes_avg = sum(g_bytes) / len(g_bytes)
     achieved = gemv_bytes_avg / (gemv_ms * 1e-3) / 1e9
-    traffic = load_traffic("k_gemv.hip", "gemv_lq19_8_70b_b1")
+    traffic = load_traffic("k_gemv1.hip", "gemv_lq19_8_70b_b1")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "gemv_lut_kernel", "bytes_per_launch": int(gemv_bytes_avg),
+                "kernel": "lq_gemv B=1 (gemv1_kernel + gemv1_reduce_kernel)",
+                "bytes_per_launch": int(gemv_bytes_avg),
                 "avg_launch_us": round(gemv_ms * 1e3, 3),
                 "per_shape_us": {f"{L.m}x{L.n}": round(per[j] * 1e3, 3)
                                  for j, L in enumerate(layers)}}
+    step(0)
+    torch.cuda.synchronize()
     outs_host = [o.cpu().numpy().copy() for o in outs]
-    rot_info = {"copies": rots[0].R, "bytes_per_copy": int(layers[0].packed.nbytes)}
+    rot_info = {"copies": rots[0].R, "bytes_per_copy": int(layers[0].packed.nbytes),
+                "timing": "HIP graph per step, replayed; checked bit for bit against eager"}
 
     gemm = None if args.only == "layer" else run_gemm(args, torch, lq, synth, dev)
     cases = None if (args.no_cases or args.only != "all") else run_cases(torch, lq, synth, dev)
     return dict(value=value, ms_step=ms_step, roofline=roofline, gemm=gemm, cases=cases,
                 layers=layers, outs=outs_host, rot=rot_info, step_bytes=step_bytes)
+
+
+def capture_graphs(torch, fns):
+    """One HIP graph per callable (captured on a side stream, as torch asks);
+    the callables must allocate nothing."""
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for fn in fns:
+            fn()                                   # eager run on the capture stream
+        torch.cuda.synchronize()
+        for fn in fns:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                fn()
+            graphs.append(g)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    return graphs
 
 
 def time_launches(torch, fn, n, st):
@@ -255,8 +292,11 @@ def run_cases(torch, lq, synth, dev):
 # ----------------------------------------------------------------- CPU baseline
 def cpu_baseline(layers, outs, seconds):
     """The float64 oracle (as it stands) on a bounded sample of the same
-    workload: whole rows of the up and down projections, chunk by chunk, until
-    about `seconds` of work; reported in the same unit as `value`."""
+    workload: whole rows of the up and down projections, chunk by chunk (each
+    chunk pays its own unpack, reconstruction, T^-1 product and dgemm), passes
+    over the layers repeated until about `seconds` of work; reported in the
+    same unit as `value`.  Each chunk's result is also checked against the
+    GPU output of the timed steps."""
     from oracle import lq_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -266,16 +306,13 @@ def cpu_baseline(layers, outs, seconds):
     total_t = 0.0
     total_bytes = 0
     rows_done = [0, 0]
+    passes = 0
     max_err = 0.0
     chunk = 1024
-    # the lift part (T^-1 and M for the whole layer) is paid once per layer
     j = 0
-    while total_t < seconds and any(r < L.m for r, L in zip(rows_done, layers)):
+    while total_t < seconds:
         L = layers[j % len(layers)]
-        r0 = rows_done[j % len(layers)]
-        if r0 >= L.m:
-            j += 1
-            continue
+        r0 = rows_done[j % len(layers)] % L.m
         rows = np.arange(r0, min(r0 + chunk, L.m))
         t0 = time.perf_counter()
         ref = O.forward(L.packed, L.K, L.M, L.t_inv, L.s, L.a, L.d, L.D, L.dtype, rows=rows)
@@ -286,12 +323,14 @@ def cpu_baseline(layers, outs, seconds):
             total_bytes += 2 * L.n * L.B + 2 * L.n * 128 + 4 * L.d * L.D
         got = outs[j % len(layers)][:, rows]
         max_err = max(max_err, O.rel_err_colmax(got, ref))
-        rows_done[j % len(layers)] = rows[-1] + 1
+        rows_done[j % len(layers)] += rows.size
         j += 1
+    passes = min(r // L.m for r, L in zip(rows_done, layers))
     gbs = total_bytes / total_t / 1e9
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"float64 oracle (unpack, W_hat = M y, T^-1 a, dgemm) on rows "
-                      f"{rows_done[0]} of 28672 (up) and {rows_done[1]} of 8192 (down), "
+            "sample": f"float64 oracle (unpack, W_hat = M y, T^-1 a, dgemm) in 1024-row "
+                      f"chunks: {rows_done[0]} rows of the up projection (28672 x 8192) and "
+                      f"{rows_done[1]} of the down (8192 x 28672), {passes} full passes, "
                       f"{total_t:.1f} s of CPU time",
             "seconds": round(total_t, 2), "gpu_vs_oracle_max_rel_err": float(f"{max_err:.3e}")}
 

@@ -387,36 +387,46 @@ __global__ void __launch_bounds__(kThreads, 1) gemv1_kernel(
 }
 
 // out[i] = s[i] * (sum over slices q of partials[i / 16][q][i % 16]), added in
-// a fixed order: a wave takes one 16-row granule, lane (part, row) = (l / 16,
-// l % 16) adds slices part, part + 4, ... in order (all its loads issued
-// before the first add: one round trip while S <= 128), then the 4 parts of
-// a row combine by a fixed tree.
+// a fixed order: P lanes share a row (P a power of two with at most 8 slices
+// per lane, so all of a lane's loads are in flight at once), lane part j adds
+// slices j, j + P, ... in order, and the P parts combine by a fixed tree.  A
+// wave covers 64 / P rows.
+template <int P>
 __global__ void __launch_bounds__(256) gemv1_reduce_kernel(const float* __restrict__ partials,
                                                            const float* __restrict__ s,
                                                            float* __restrict__ out, int64_t m,
                                                            int S) {
+  constexpr int R = 64 / P;                     // rows per wave
   const int lane = threadIdx.x & 63;
-  const int64_t g = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
-  const int rr = lane & 15;
-  const int part = lane >> 4;
-  const int64_t row = g * kGranuleRows + rr;
-  const float* p = partials + (g * S) * kGranuleRows + rr;
+  const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+  const int part = lane % P;
+  const int64_t row = wave * R + lane / P;
   float sum = 0.f;
   if (row < m) {
-    for (int q0 = part; q0 < S; q0 += 4 * 32) {
-      float v[32];
+    const float* p = partials + ((row >> 4) * S) * kGranuleRows + (row & 15);
+    for (int q0 = part; q0 < S; q0 += 8 * P) {
+      float v[8];
 #pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        const int q = q0 + 4 * u;
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 + u * P;
         v[u] = q < S ? p[(int64_t)q * kGranuleRows] : 0.f;
       }
 #pragma unroll
-      for (int u = 0; u < 32; ++u) sum += v[u];
+      for (int u = 0; u < 8; ++u) sum += v[u];
     }
   }
-  sum += __shfl_xor(sum, 16);
-  sum += __shfl_xor(sum, 32);
+#pragma unroll
+  for (int o = 1; o < P; o <<= 1) sum += __shfl_xor(sum, o);
   if (row < m && part == 0) out[row] = s[row] * sum;
+}
+
+template <int P>
+static void launch_reduce(const float* partials, const float* s, float* out, int64_t m, int S,
+                          hipStream_t st) {
+  constexpr int rows_per_block = 4 * (64 / P);
+  hipLaunchKernelGGL(gemv1_reduce_kernel<P>,
+                     dim3(static_cast<unsigned>((m + rows_per_block - 1) / rows_per_block)),
+                     dim3(256), 0, st, partials, s, out, m, S);
 }
 
 // Ranges of the workgroups over the (slice, granule) order.  A range that
@@ -477,8 +487,17 @@ hipError_t launch_gemv1(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, co
                        a_lift, out, partials, sc, w_bytes, a_bytes);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gemv1_reduce_kernel, dim3(static_cast<unsigned>((sc.NG + 3) / 4)),
-                       dim3(256), 0, st, partials, s, out, m, sc.S);
+    const int need = (sc.S + 7) / 8;            // parts so that each adds <= 8 slices
+    if (need <= 1)
+      launch_reduce<1>(partials, s, out, m, sc.S, st);
+    else if (need <= 2)
+      launch_reduce<2>(partials, s, out, m, sc.S, st);
+    else if (need <= 4)
+      launch_reduce<4>(partials, s, out, m, sc.S, st);
+    else if (need <= 8)
+      launch_reduce<8>(partials, s, out, m, sc.S, st);
+    else
+      launch_reduce<16>(partials, s, out, m, sc.S, st);
   }
   return hipGetLastError();
 }

@@ -2,11 +2,17 @@
 // 关键设计 4: the small transform of the activations done once per input;
 // 关键设计 1 for the per-group M).  float32 accumulation throughout.
 //
-// One workgroup owns a run of whole groups (about 128 channels of u) and a
-// chunk of tokens.  It stages the activation blocks its channels read in LDS,
-// computes those u channels (each u channel is one 128-long dot product with a
-// row of its T^-1 block, so groups that straddle two blocks need no special
-// case), keeps u in LDS, and writes the lifted values of its groups.
+// One workgroup owns a run of whole groups (about 32 channels of u, one
+// group when d > 32) and a
+// chunk of up to 16 tokens.  The T^-1 rows of its channels are contiguous in
+// memory ([n/128][128][128], row r of block q is channel 128q + r), so it
+// reads them with coalesced 16-byte loads, all issued before the first use:
+// 16 lanes per row, 8 elements each.  Each lane dots its 8 elements with the
+// matching activations (staged in LDS as float32), the 16 lanes of a row are
+// combined by a shuffle tree, u goes to LDS, and the workgroup writes the
+// lifted values of its groups (consecutive threads, consecutive positions).
+// Groups may straddle two 128-blocks: each row reads the activations of its
+// own block.
 #include "lq_internal.h"
 
 namespace lq {
@@ -48,103 +54,116 @@ __device__ __forceinline__ void load8_as_float<LQ_F32>(const void* base, int64_t
   v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
 }
 
-// TBMAX: tokens handled per workgroup (compile-time bound of the register block).
-template <int A_DT, int T_DT, int O_DT, int TBMAX>
+constexpr int kMaxRows = 64;                     // channels of u per workgroup (d <= 64)
+constexpr int kPasses = kMaxRows / 16;           // 16 rows per pass of 256 threads
+
+// TB: tokens per workgroup (1, 2, 4, 8 or 16).
+template <int A_DT, int T_DT, int O_DT, int TB>
 __global__ void __launch_bounds__(kThreads) lift_kernel(const void* __restrict__ a,
                                                         const void* __restrict__ t_inv,
                                                         const float* __restrict__ M,
                                                         void* __restrict__ out, int B, int n,
                                                         int d, int D, int GW) {
   extern __shared__ float smem[];
+  float* sa = smem;                              // [TB][256] activations of <= 2 blocks
+  float* su = sa + TB * 2 * kTB;                 // [TB][kMaxRows] transformed
+  float* sM = su + TB * kMaxRows;                // [d][D]
+
   const int G = n / d;
-  const int K = G * D;
+  const int64_t K = (int64_t)G * D;
   const int g0 = blockIdx.x * GW;
   const int gcount = min(GW, G - g0);
   const int c0 = g0 * d;
-  const int cw = gcount * d;                     // channels of u owned here
+  const int cw = gcount * d;                     // channels of u owned here (<= kMaxRows)
   const int blk0 = c0 / kTB;
-  const int nblk = (c0 + cw - 1) / kTB - blk0 + 1;
-  const int b0 = blockIdx.y * TBMAX;
-  const int bc = min(TBMAX, B - b0);
-
-  float* sa = smem;                              // [TBMAX][nblk*128] activations
-  float* su = sa + TBMAX * nblk * kTB;           // [TBMAX][cw] transformed
-  float* sM = su + TBMAX * cw;                   // [d][D]
-
+  const int nblk = (c0 + cw - 1) / kTB - blk0 + 1;   // 1 or 2
+  const int b0 = blockIdx.y * TB;
+  const int bc = min(TB, B - b0);
   const int tid = threadIdx.x;
+
+  // T^-1 rows c0 .. c0 + cw - 1: lane j of a row loads elements 8j .. 8j + 7
+  const int j = tid & 15;
+  float tv[kPasses][8];
+#pragma unroll
+  for (int p = 0; p < kPasses; ++p) {
+    const int row = p * 16 + (tid >> 4);
+    if (row < cw) {
+      load8_as_float<T_DT>(t_inv, (int64_t)(c0 + row) * kTB + 8 * j, tv[p]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) tv[p][e] = 0.f;
+    }
+  }
   const int aw = nblk * kTB;
   for (int i = tid; i < bc * aw; i += kThreads) {
     const int b = i / aw;
-    const int j = i - b * aw;
-    sa[b * aw + j] = load_as_float<A_DT>(a, (int64_t)(b0 + b) * n + blk0 * kTB + j);
+    const int k = i - b * aw;
+    sa[b * 2 * kTB + k] = load_as_float<A_DT>(a, (int64_t)(b0 + b) * n + blk0 * kTB + k);
   }
   for (int i = tid; i < d * D; i += kThreads) sM[i] = M[i];
   __syncthreads();
 
-  // u: thread (c, half) owns channel c0 + c and tokens b = half, half + H, ...
-  constexpr int H = kThreads / kTB;              // 2 threads per channel
-  const int c = tid % kTB;
-  const int half = tid / kTB;
-  if (c < cw) {
-    const int ch = c0 + c;
-    const int q = ch / kTB;
-    const int r = ch - q * kTB;
-    const int aoff = (q - blk0) * kTB;
-    const int64_t trow = ((int64_t)q * kTB + r) * kTB;
-    constexpr int NB = (TBMAX + H - 1) / H;
-    float acc[NB];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) acc[i] = 0.f;
-    for (int j = 0; j < kTB; j += 8) {
-      float tv[8];
-      load8_as_float<T_DT>(t_inv, trow + j, tv);
+  for (int p = 0; p < kPasses; ++p) {
+    if (p * 16 >= cw) break;                     // workgroup-uniform
+    const int row = p * 16 + (tid >> 4);
+    const int q = (c0 + row) / kTB - blk0;       // block of this row, relative
+    float acc[TB];
 #pragma unroll
-      for (int i = 0; i < NB; ++i) {
-        const int b = half + H * i;
-        if (b < bc) {
-          const float* ab = sa + b * aw + aoff + j;
+    for (int b = 0; b < TB; ++b) {
+      const float* ab = sa + b * 2 * kTB + q * kTB + 8 * j;
+      float s0 = 0.f;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[i] = fmaf(tv[e], ab[e], acc[i]);
-        }
-      }
+      for (int e = 0; e < 8; ++e) s0 = fmaf(tv[p][e], ab[e], s0);
+      acc[b] = s0;
     }
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int b = half + H * i;
-      if (b < bc) su[b * cw + c] = acc[i];
+    for (int b = 0; b < TB; ++b) {
+      float v = acc[b];
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 8);
+      if (j == 0 && row < cw && b < bc) su[b * kMaxRows + row] = v;
     }
   }
   __syncthreads();
 
-  // a_hat for the groups of this workgroup: consecutive threads write
-  // consecutive lifted positions of one token.
+  // a_hat for the groups of this workgroup
   const int ow = gcount * D;
   for (int i = tid; i < bc * ow; i += kThreads) {
     const int b = i / ow;
     const int rem = i - b * ow;
     const int g = rem / D;
     const int jj = rem - g * D;
-    const float* ub = su + b * cw + g * d;
+    const float* ub = su + b * kMaxRows + g * d;
     float acc = 0.f;
     for (int rr = 0; rr < d; ++rr) acc = fmaf(sM[rr * D + jj], ub[rr], acc);
     store_from_float<O_DT>(out, (int64_t)(b0 + b) * K + (int64_t)g0 * D + rem, acc);
   }
 }
 
+template <int A_DT, int T_DT, int O_DT, int TB>
+hipError_t launch_lift_tb(const void* a, int64_t B, int64_t n, const void* t_inv, const float* M,
+                          int d, int D, void* out, hipStream_t st) {
+  const int G = static_cast<int>(n / d);
+  const int GW = 32 / d > 0 ? 32 / d : 1;        // whole groups: <= 32 channels, or one group
+  const int gx = (G + GW - 1) / GW;
+  const int gy = static_cast<int>((B + TB - 1) / TB);
+  const size_t lds = sizeof(float) * (TB * 2 * kTB + TB * kMaxRows + d * D);
+  hipLaunchKernelGGL((lift_kernel<A_DT, T_DT, O_DT, TB>), dim3(gx, gy), dim3(kThreads), lds, st,
+                     a, t_inv, M, out, static_cast<int>(B), static_cast<int>(n), d, D, GW);
+  return hipGetLastError();
+}
+
 template <int A_DT, int T_DT, int O_DT>
 hipError_t launch_lift_t(const void* a, int64_t B, int64_t n, const void* t_inv, const float* M,
                          int d, int D, void* out, hipStream_t st) {
-  const int G = static_cast<int>(n / d);
-  const int GW = kTB / d > 0 ? kTB / d : 1;           // about 128 channels per workgroup
-  const int gx = (G + GW - 1) / GW;
-  const int cwmax = GW * d;
-  const int nblk = 2;                                 // cw <= 128 spans at most 2 blocks
-  constexpr int TBMAX = 16;
-  const int gy = static_cast<int>((B + TBMAX - 1) / TBMAX);
-  const size_t lds = sizeof(float) * (TBMAX * nblk * kTB + TBMAX * cwmax + d * D);
-  hipLaunchKernelGGL((lift_kernel<A_DT, T_DT, O_DT, TBMAX>), dim3(gx, gy), dim3(kThreads), lds,
-                     st, a, t_inv, M, out, static_cast<int>(B), static_cast<int>(n), d, D, GW);
-  return hipGetLastError();
+  if (B <= 1) return launch_lift_tb<A_DT, T_DT, O_DT, 1>(a, B, n, t_inv, M, d, D, out, st);
+  if (B <= 2) return launch_lift_tb<A_DT, T_DT, O_DT, 2>(a, B, n, t_inv, M, d, D, out, st);
+  if (B <= 4) return launch_lift_tb<A_DT, T_DT, O_DT, 4>(a, B, n, t_inv, M, d, D, out, st);
+  if (B <= 8) return launch_lift_tb<A_DT, T_DT, O_DT, 8>(a, B, n, t_inv, M, d, D, out, st);
+  return launch_lift_tb<A_DT, T_DT, O_DT, 16>(a, B, n, t_inv, M, d, D, out, st);
 }
 
 template <int A_DT, int T_DT>

@@ -81,6 +81,13 @@ def words_per_row(K: int) -> int:
     return (K + 31) // 32
 
 
+def aligned_row_words(K: int) -> int:
+    """Row stride in words that starts every row on a 128-byte line (the
+    default for generated layers: rows whose slices straddle lines are read
+    twice over by a slice-wise stream)."""
+    return (words_per_row(K) + 31) // 32 * 32
+
+
 # ---------------------------------------------------------------- 16-bit storage
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bit patterns (uint16), round to nearest even (finite input)."""
@@ -104,18 +111,18 @@ def random_sign_words(rng: np.random.Generator, rows: int, K: int,
                       ldw: Optional[int] = None) -> np.ndarray:
     """Bernoulli(0.5) signs drawn directly as packed words: uint32 [rows][ldw].
     Every bit of a uniform random word is an independent fair coin; bits at
-    positions >= K (and whole padding words) are cleared."""
-    ldw = words_per_row(K) if ldw is None else ldw
-    if ldw < words_per_row(K):
+    positions >= K and the padding words up to ldw are zero.  Only the
+    ceil(K/32) data words of each row are drawn, so the values do not depend
+    on ldw."""
+    nw = words_per_row(K)
+    ldw = nw if ldw is None else ldw
+    if ldw < nw:
         raise ValueError("ldw too small")
-    w = rng.integers(0, 2**32, size=(rows, ldw), dtype=np.uint64).astype(np.uint32)
-    full = K // 32
-    rem = K % 32
-    if rem:
-        w[:, full] &= np.uint32((1 << rem) - 1)
-        w[:, full + 1:] = 0
-    else:
-        w[:, full:] = 0
+    data = rng.integers(0, 2**32, size=(rows, nw), dtype=np.uint64).astype(np.uint32)
+    if K % 32:
+        data[:, -1] &= np.uint32((1 << (K % 32)) - 1)
+    w = np.zeros((rows, ldw), dtype=np.uint32)
+    w[:, :nw] = data
     return w
 
 
@@ -169,7 +176,7 @@ def make_layer(m: int, n: int, d: int, D: int, B: int, seed: int, dtype: str = "
         raise ValueError("n must be a multiple of the transform block")
     K = lifted_dim(n, d, D)
     rng = np.random.default_rng(seed)
-    packed = random_sign_words(rng, m, K, ldw)
+    packed = random_sign_words(rng, m, K, aligned_row_words(K) if ldw is None else ldw)
     M = (rng.standard_normal((d, D)) / np.sqrt(D)).astype(np.float32)
     nb = n // t_block
     if identity_t:

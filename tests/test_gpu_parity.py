@@ -73,7 +73,8 @@ def test_pack_empty_is_noop(dev):
 LIFT_CASES = [  # (n, d, D, B, act dtype)
     (1280, 10, 24, 1, "f16"), (640, 10, 24, 3, "bf16"), (1024, 8, 19, 1, "bf16"),
     (512, 8, 20, 16, "bf16"), (256, 16, 40, 33, "bf16"), (384, 8, 16, 4, "f16"),
-    (384, 3, 7, 2, "bf16"), (256, 64, 128, 1, "f16"),
+    (384, 3, 7, 2, "bf16"), (256, 64, 128, 1, "f16"), (1280, 40, 100, 2, "bf16"),
+    (640, 32, 80, 20, "f16"),
 ]
 
 
@@ -103,7 +104,7 @@ def test_lift_16bit_outputs(dev, odt):
 # ----------------------------------------------------------------- GEMV (lifted product)
 GEMV_CASES = [  # (m, K, B): ragged rows, slices and token groups
     (1, 4, 1), (63, 512, 1), (65, 516, 1), (200, 1544, 2), (129, 3072, 3), (300, 2048, 4),
-    (77, 1000, 5), (1000, 4100, 16), (4096, 10240, 1), (520, 9216, 7),
+    (77, 1000, 5), (1000, 4100, 16), (4096, 10240, 1), (520, 9216, 7), (200, 40960, 1),
     # one token: a single slice (no split), a 4-position last slice, a ragged
     # 8-row granule, and more slices than workgroups (ranges over > 2 slices)
     (1000, 1024, 1), (37, 1028, 1), (8193, 2048, 1), (64, 300000, 1),
