@@ -8,7 +8,7 @@
 // v_mfma_f32_32x32x16; the lifted activations are the B operand, staged
 // through LDS.  Accumulation is float32.
 //
-// Expansion of one weight byte (8 lifted positions of one row, the A operand
+// Expansion of one weight byte (8 lifted positions of one row: the A operand
 // of one lane for one MFMA) into four dwords of two 16-bit values:
 //   rep = byte | byte << 16                (v_perm_b32)
 //   h   = rep << (15-2p, 14-2p) per half   (v_pk_lshlrev_b16: bit 2p -> bit 15,
@@ -17,10 +17,33 @@
 // A set bit sets the sign, so the tile holds -sigma; the epilogue multiplies
 // by -s.
 //
-// Tiling: 128 rows x 128 tokens per workgroup, 4 waves in 2 x 2, each wave
-// 64 x 64 (2 x 2 MFMA tiles of 32 x 32), k-step 32 per main-loop iteration,
-// activations double-buffered in LDS.
+// Tiling: 128 rows x 128 tokens per workgroup of 8 waves.  The lifted
+// dimension advances 256 positions per step; wave w takes rows
+// 64 (w % 2) .. +63 of the tile against all 128 tokens (2 x 4 MFMA tiles:
+// each expanded weight byte feeds four MFMAs, each activation fragment read
+// from LDS two) on quarter w / 2 of every step's positions.  The four
+// quarters are summed through LDS at the end, where the tile is also
+// transposed so that the output rows are written with consecutive lanes on
+// consecutive addresses.
+//
+// The k order inside a quarter-step is permuted the same way for both
+// operands: sub-step c (c < 4) gives lane (row or token, h) positions
+// 8 (8 kq + 4 h + c) .. +7 of the step, so a lane's weight bits for a whole
+// quarter-step are one dword of its row.  Weight dwords are loaded several
+// steps ahead into a ring of registers; the activations of the next step
+// (128 tokens x 256 positions) are loaded into registers at the start of a
+// step and written at its end to the other of two LDS buffers.  Inside a
+// step the expansion of sub-step c + 1's weights and the LDS reads of its
+// activations are issued between the MFMAs of sub-step c.  All global loads
+// are buffer loads whose range check returns zeros for rows, tokens and
+// positions past the end, so the loop has no branches.
+//
+// Workgroups are ordered so that the ones on one XCD (dispatched round-robin
+// over 8) take a contiguous run of tiles in token-tile-major order and share
+// the token tile's activations in that XCD's L2.
 #include "lq_internal.h"
+
+#include <type_traits>
 
 namespace lq {
 namespace {
@@ -30,11 +53,19 @@ typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBM = 128;
-constexpr int kBN = 128;
-constexpr int kBK = 32;
-constexpr int kThreads = 256;
-constexpr int kLdsRow = kBK + 8;   // 16-bit elements per LDS row (80 B: conflict-free b128 reads)
+constexpr int kBM = 128;                 // rows per workgroup
+constexpr int kBN = 128;                 // tokens per workgroup
+constexpr int kKS = 256;                 // lifted positions per step
+constexpr int kThreads = 512;            // 8 waves: 2 row halves x 4 position quarters
+constexpr int kRing = 4;                 // steps of weight dwords held in registers
+constexpr int kLdsRow = kKS + 8;         // 16-bit elements per LDS token row (528 B)
+constexpr int kBufElems = kBN * kLdsRow; // one activation buffer (66 KB)
+constexpr int kOutLd = kBM + 4;          // floats per token row of the epilogue tile
+constexpr int kBChunks = kBN * kKS / 8 / kThreads;   // 16-byte activation chunks per thread
+constexpr uint32_t kNoLoad = 0x80000000u;  // an offset past every buffer's range
+constexpr uint32_t kRsrcWord3 = 0x00020000u;
+
+static_assert(kBN * kOutLd * 4 <= 2 * kBufElems * 2, "epilogue tile must fit the LDS buffers");
 
 template <int DT>
 struct Mfma;
@@ -61,9 +92,15 @@ struct Mfma<LQ_BF16> {
   }
 };
 
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t one) {
+  uint32_t d;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(x), "s"(mask), "v"(one));
+  return d;
+}
+
 // Byte `byte_idx` of `word` -> 8 16-bit values -sigma (bit 1 -> -1, bit 0 -> +1).
 template <int DT>
-__device__ __forceinline__ uint4 expand_byte(uint32_t word, int byte_idx) {
+__device__ __forceinline__ uint4 expand_byte(uint32_t word, int byte_idx, uint32_t one) {
   const uint32_t selr = static_cast<uint32_t>(byte_idx) | 0x0C000C00u |
                         (static_cast<uint32_t>(byte_idx) << 16);
   const uint32_t rep = __builtin_amdgcn_perm(0u, word, selr);   // [x, 0, x, 0]
@@ -76,122 +113,206 @@ __device__ __forceinline__ uint4 expand_byte(uint32_t word, int byte_idx) {
     const us2 h = r << sh;
     uint32_t hv;
     __builtin_memcpy(&hv, &h, 4);
-    d[p] = (hv & 0x80008000u) | Mfma<DT>::kOneOne;
+    d[p] = and_or(hv, 0x80008000u, one);
   }
   return make_uint4(d[0], d[1], d[2], d[3]);
 }
 
 template <int DT>
-__global__ void __launch_bounds__(kThreads) gemm_mfma_kernel(
-    const uint32_t* __restrict__ w, int m, int K, int64_t ldw, const float* __restrict__ s,
-    const uint16_t* __restrict__ ah, int B, float* __restrict__ out) {
-  __shared__ uint16_t sB[2][kBN * kLdsRow];
+__global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(
+    const uint32_t* __restrict__ w, int m, int K, int ldw, const float* __restrict__ s,
+    const uint16_t* __restrict__ ah, int B, float* __restrict__ out, int tiles_m, int tiles_n) {
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2 * kBufElems];   // 132 KB
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
-  const int row0 = blockIdx.x * kBM;
-  const int tok0 = blockIdx.y * kBN;
-  const int hi = lane >> 5;         // k-half of the MFMA operands
+  const int wr = wave & 1;           // 64-row half of the tile
+  const int kq = wave >> 1;          // quarter of each step's positions
+  const int h = lane >> 5;
   const int l32 = lane & 31;
 
-  // activation tile loader: thread -> (token, 16 k)
-  const int ld_tok = tid >> 1;
-  const int ld_k = (tid & 1) * 16;
-  const bool tok_ok = (tok0 + ld_tok) < B;
-  const uint16_t* ah_row = ah + (int64_t)(tok0 + ld_tok) * K;
+  // Workgroup wg runs on XCD wg % 8; XCD x takes the tiles
+  // [x * per_x, (x + 1) * per_x) in token-tile-major order.
+  const int wg = blockIdx.x;
+  const int per_x = (tiles_m * tiles_n + 7) / 8;
+  const int lin = (wg & 7) * per_x + (wg >> 3);
+  if (lin >= tiles_m * tiles_n) return;
+  const int tn = lin / tiles_m;
+  const int tm = lin - tn * tiles_m;
+  const int row0 = tm * kBM;
+  const int tok0 = tn * kBN;
+  const int rows = min(kBM, m - row0);
+  const int toks = min(kBN, B - tok0);
 
-  // weight rows of this lane (A operand rows of the two 32-row MFMA tiles)
-  const int64_t arow0 = row0 + wm * 64 + l32;
-  const int64_t arow1 = arow0 + 32;
-  const bool ar0 = arow0 < m, ar1 = arow1 < m;
-  const uint32_t* wr0 = w + arow0 * ldw;
-  const uint32_t* wr1 = w + arow1 * ldw;
-
-  f32x16 acc[2][2];
+  // Weights: rows row0 .. row0 + rows - 1.  Offsets stay below 2^31
+  // (ldw <= 2^22): a dword past the row's end pairs with zero activations,
+  // rows past m fall outside the range and read as zero.
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(w + static_cast<int64_t>(row0) * ldw), (short)0,
+      static_cast<int>(static_cast<uint32_t>(rows) * static_cast<uint32_t>(ldw) * 4u), kRsrcWord3);
+  uint32_t a_off[2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int mi = 0; mi < 2; ++mi)
+    a_off[mi] = (static_cast<uint32_t>(wr * 64 + mi * 32 + l32) * ldw + 2 * kq + h) * 4u;
+  auto load_a = [&](int step, uint32_t (&a)[2]) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int mi = 0; mi < 2; ++mi)
+      a[mi] = __builtin_amdgcn_raw_buffer_load_b32(wres, a_off[mi], step * (kKS / 8), 0);
+  };
+
+  // Activations: tokens tok0 .. tok0 + toks - 1; a step is 128 tokens x 32
+  // chunks of 8 positions, kBChunks per thread.  Chunks at positions >= K
+  // (K % 8 == 0) take the out-of-range offset; tokens past B fall outside
+  // the range.
+  const __amdgpu_buffer_rsrc_t bres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(ah + static_cast<int64_t>(tok0) * K), (short)0,
+      static_cast<int>(static_cast<uint32_t>(toks) * static_cast<uint32_t>(K) * 2u), kRsrcWord3);
+  const int b_kk = (tid & 31) * 8;
+  const int b_tok = tid >> 5;
+  const uint32_t b_off = (static_cast<uint32_t>(b_tok) * K + b_kk) * 2u;
+  const uint32_t b_tok_stride = static_cast<uint32_t>(kThreads / 32) * K * 2u;
+  // per lane only the range test; the step and the token stride go in the
+  // scalar offset (kNoLoad + soffset stays below 2^32 and out of range)
+  auto load_b = [&](int step, uint4 (&v)[kBChunks]) {
+    const uint32_t vo = step * kKS + b_kk < K ? b_off : kNoLoad;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  const int ktiles = (K + kBK - 1) / kBK;
-
-  auto load_b = [&](int kt, uint4& v0, uint4& v1) {
-    const int k = kt * kBK + ld_k;
-    v0 = make_uint4(0, 0, 0, 0);
-    v1 = make_uint4(0, 0, 0, 0);
-    if (tok_ok) {
-      if (k + 8 <= K) v0 = *reinterpret_cast<const uint4*>(ah_row + k);
-      if (k + 16 <= K) v1 = *reinterpret_cast<const uint4*>(ah_row + k + 8);
+    for (int i = 0; i < kBChunks; ++i) {
+      const auto r = __builtin_amdgcn_raw_buffer_load_b128(
+          bres, vo, static_cast<int>(i * b_tok_stride + static_cast<uint32_t>(step * kKS * 2)), 0);
+      __builtin_memcpy(&v[i], &r, 16);
     }
   };
-  auto store_b = [&](int buf, const uint4& v0, const uint4& v1) {
-    uint4* dst = reinterpret_cast<uint4*>(&sB[buf][ld_tok * kLdsRow + ld_k]);
-    dst[0] = v0;
-    dst[1] = v1;
-  };
-  auto load_a = [&](int kt, uint32_t& a0, uint32_t& a1) {
-    const int64_t wc = kt;            // one 32-bit word = 32 lifted positions = one k-tile
-    a0 = (ar0 && wc < ldw) ? wr0[wc] : 0u;
-    a1 = (ar1 && wc < ldw) ? wr1[wc] : 0u;
+  uint16_t* const b_st = &sB[b_tok * kLdsRow + b_kk];
+  auto store_b = [&](int buf, const uint4 (&v)[kBChunks]) {
+#pragma unroll
+    for (int i = 0; i < kBChunks; ++i)
+      *reinterpret_cast<uint4*>(b_st + buf * kBufElems + i * (kThreads / 32) * kLdsRow) = v[i];
   };
 
-  uint4 nb0, nb1;
-  uint32_t na0, na1;
-  load_b(0, nb0, nb1);
-  load_a(0, na0, na1);
-  store_b(0, nb0, nb1);
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < 4; ++nj)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[mi][nj][e] = 0.f;
+
+  // LDS element offset of this lane's activation fragment (token block 0,
+  // sub-step 0) in buffer 0
+  const uint16_t* const b_frag = &sB[l32 * kLdsRow + 8 * (8 * kq + 4 * h)];
+  auto read_b = [&](int buf, int c, uint4 (&bf)[4]) {
+#pragma unroll
+    for (int nj = 0; nj < 4; ++nj)
+      bf[nj] = *reinterpret_cast<const uint4*>(b_frag + buf * kBufElems + nj * 32 * kLdsRow + 8 * c);
+  };
+  const uint32_t one = Mfma<DT>::kOneOne;
+
+  const int steps = (K + kKS - 1) / kKS;
+  uint32_t a[kRing][2];
+  uint4 nb[kBChunks];
+#pragma unroll
+  for (int r = 0; r < kRing; ++r) load_a(r, a[r]);
+  __builtin_amdgcn_sched_barrier(0);
+  load_b(0, nb);
+  __builtin_amdgcn_sched_barrier(0);
+  store_b(0, nb);
   __syncthreads();
 
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int buf = kt & 1;
-    const uint32_t wa0 = na0, wa1 = na1;
-    if (kt + 1 < ktiles) {
-      load_b(kt + 1, nb0, nb1);
-      load_a(kt + 1, na0, na1);
-    }
+  // One step, st % kRing == P: a[P] holds this step's weight dwords, LDS
+  // buffer P % 2 its activations.  The scheduling barriers keep the phases in
+  // this order: the next step's activation loads first, then per sub-step the
+  // MFMAs with the next sub-step's expansion and LDS reads, the weight
+  // loads kRing steps ahead right after the last expansion of a[P] (so they
+  // land in its registers), the LDS store of the next step's activations last.
+  auto step = [&](auto P, int st) {
+    constexpr int p = decltype(P)::value;
+    constexpr int buf = p & 1;
+    load_b(st + 1, nb);
+    uint4 bf[4];
+    uint4 af[2], afn[2];
+    read_b(buf, 0, bf);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      // B operands: token tok = wn*64 + ni*32 + l32, k = kk*16 + hi*8 .. +8
-      uint4 bf[2];
+    for (int mi = 0; mi < 2; ++mi) af[mi] = expand_byte<DT>(a[p][mi], 0, one);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        const int tok = wn * 64 + ni * 32 + l32;
-        bf[ni] = *reinterpret_cast<const uint4*>(&sB[buf][tok * kLdsRow + kk * 16 + hi * 8]);
+    for (int c = 0; c < 4; ++c) {
+      if (c == 3) {
+        load_a(st + kRing, a[p]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      const int byte_idx = kk * 2 + hi;   // lifted positions kk*16 + hi*8 .. +8 of the word
-      const uint4 af0 = expand_byte<DT>(wa0, byte_idx);
-      const uint4 af1 = expand_byte<DT>(wa1, byte_idx);
-      acc[0][0] = Mfma<DT>::run(af0, bf[0], acc[0][0]);
-      acc[0][1] = Mfma<DT>::run(af0, bf[1], acc[0][1]);
-      acc[1][0] = Mfma<DT>::run(af1, bf[0], acc[1][0]);
-      acc[1][1] = Mfma<DT>::run(af1, bf[1], acc[1][1]);
+      if (c < 3) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) afn[mi] = expand_byte<DT>(a[p][mi], c + 1, one);
+      }
+      // token block nj's fragment is reloaded for sub-step c + 1 as soon as
+      // its two MFMAs of sub-step c are issued
+#pragma unroll
+      for (int nj = 0; nj < 4; ++nj) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) acc[mi][nj] = Mfma<DT>::run(af[mi], bf[nj], acc[mi][nj]);
+        if (c < 3)
+          bf[nj] = *reinterpret_cast<const uint4*>(b_frag + buf * kBufElems + nj * 32 * kLdsRow +
+                                                   8 * (c + 1));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (c < 3) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) af[mi] = afn[mi];
+      }
     }
-    if (kt + 1 < ktiles) {
-      store_b(buf ^ 1, nb0, nb1);
-      __syncthreads();
-    }
+    store_b(buf ^ 1, nb);
+    __syncthreads();
+  };
+  // A whole number of ring turns, without branches inside the loop body: a
+  // step past the end reads zero activations and adds nothing.
+  for (int st = 0; st < steps; st += kRing) {
+    step(std::integral_constant<int, 0>{}, st);
+    step(std::integral_constant<int, 1>{}, st + 1);
+    step(std::integral_constant<int, 2>{}, st + 2);
+    step(std::integral_constant<int, 3>{}, st + 3);
   }
 
-  // epilogue: D[i][j], i = row within the 32x32 tile, j = token; lane holds
-  // j = l32 and rows 8*(e/4) + 4*hi + (e%4) for e = 0..15.
+  // Epilogue: D[i][j] of a 32 x 32 MFMA tile, i = row, j = token; lane holds
+  // j = l32 and rows 8 (e / 4) + 4 h + (e % 4), e = 0..15.  Quarter 0 writes
+  // its sums to the [token][row] tile in LDS, quarters 1..3 add theirs in
+  // turn, then every thread scales and stores one row of the output for
+  // every fourth token.
+  float* tile = reinterpret_cast<float*>(&sB[0]);
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
+  for (int qt = 0; qt < 4; ++qt) {
+    if (kq == qt) {
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int tok = tok0 + wn * 64 + ni * 32 + l32;
-      if (tok >= B) continue;
-      float* orow = out + (int64_t)tok * m;
+      for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = row0 + wm * 64 + mi * 32 + 8 * (e >> 2) + 4 * hi + (e & 3);
-        if (row < m) orow[row] = -s[row] * acc[mi][ni][e];
-      }
+        for (int nj = 0; nj < 4; ++nj) {
+          const int tok = nj * 32 + l32;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int row = wr * 64 + mi * 32 + 8 * g + 4 * h;
+            float4* dst = reinterpret_cast<float4*>(&tile[tok * kOutLd + row]);
+            float4 v = make_float4(acc[mi][nj][4 * g], acc[mi][nj][4 * g + 1],
+                                   acc[mi][nj][4 * g + 2], acc[mi][nj][4 * g + 3]);
+            if (qt > 0) {
+              const float4 o = *dst;
+              v.x += o.x;
+              v.y += o.y;
+              v.z += o.z;
+              v.w += o.w;
+            }
+            *dst = v;
+          }
+        }
     }
+    __syncthreads();
+  }
+  const int row = tid & (kBM - 1);
+  if (row < rows) {
+    const float ns = -s[row0 + row];
+    float* orow = out + static_cast<int64_t>(tok0) * m + row0 + row;
+#pragma unroll 4
+    for (int t = tid >> 7; t < toks; t += kThreads / kBM)
+      orow[static_cast<int64_t>(t) * m] = ns * tile[t * kOutLd + row];
   }
 }
 
@@ -199,17 +320,19 @@ __global__ void __launch_bounds__(kThreads) gemm_mfma_kernel(
 
 hipError_t launch_gemm(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
                        const void* a_lift, lq_dtype dt, int64_t B, float* out, hipStream_t st) {
-  const dim3 grid(static_cast<unsigned>((m + kBM - 1) / kBM),
-                  static_cast<unsigned>((B + kBN - 1) / kBN));
+  const int tiles_m = static_cast<int>((m + kBM - 1) / kBM);
+  const int tiles_n = static_cast<int>((B + kBN - 1) / kBN);
+  const int per_x = (tiles_m * tiles_n + 7) / 8;
+  const dim3 grid(static_cast<unsigned>(8 * per_x));
   const uint16_t* ah = static_cast<const uint16_t*>(a_lift);
   if (dt == LQ_F16)
     hipLaunchKernelGGL(gemm_mfma_kernel<LQ_F16>, grid, dim3(kThreads), 0, st, w,
-                       static_cast<int>(m), static_cast<int>(K), ldw, s, ah, static_cast<int>(B),
-                       out);
+                       static_cast<int>(m), static_cast<int>(K), static_cast<int>(ldw), s, ah,
+                       static_cast<int>(B), out, tiles_m, tiles_n);
   else
     hipLaunchKernelGGL(gemm_mfma_kernel<LQ_BF16>, grid, dim3(kThreads), 0, st, w,
-                       static_cast<int>(m), static_cast<int>(K), ldw, s, ah, static_cast<int>(B),
-                       out);
+                       static_cast<int>(m), static_cast<int>(K), static_cast<int>(ldw), s, ah,
+                       static_cast<int>(B), out, tiles_m, tiles_n);
   return hipGetLastError();
 }
 

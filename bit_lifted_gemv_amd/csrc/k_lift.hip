@@ -94,13 +94,44 @@ __global__ void __launch_bounds__(kThreads) lift_kernel(const void* __restrict__
       for (int e = 0; e < 8; ++e) tv[p][e] = 0.f;
     }
   }
+  // Activations of the (one or two) blocks for bc tokens, 8 elements per
+  // 16-byte load, and M: every load is issued before the first LDS store.
   const int aw = nblk * kTB;
-  for (int i = tid; i < bc * aw; i += kThreads) {
-    const int b = i / aw;
-    const int k = i - b * aw;
-    sa[b * 2 * kTB + k] = load_as_float<A_DT>(a, (int64_t)(b0 + b) * n + blk0 * kTB + k);
+  const int avec = bc * (aw / 8);
+  constexpr int kAPer = (TB * 2 * kTB / 8 + kThreads - 1) / kThreads;
+  float av[kAPer][8];
+#pragma unroll
+  for (int k = 0; k < kAPer; ++k) {
+    const int i = tid + k * kThreads;
+    if (i < avec) {
+      const int b = i / (aw / 8);
+      const int col = (i - b * (aw / 8)) * 8;
+      load8_as_float<A_DT>(a, (int64_t)(b0 + b) * n + blk0 * kTB + col, av[k]);
+    }
   }
-  for (int i = tid; i < d * D; i += kThreads) sM[i] = M[i];
+  for (int i0 = 0; i0 < d * D; i0 += 8 * kThreads) {
+    float mv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kThreads + tid;
+      mv[u] = i < d * D ? M[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = i0 + u * kThreads + tid;
+      if (i < d * D) sM[i] = mv[u];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < kAPer; ++k) {
+    const int i = tid + k * kThreads;
+    if (i < avec) {
+      const int b = i / (aw / 8);
+      const int col = (i - b * (aw / 8)) * 8;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sa[b * 2 * kTB + col + e] = av[k][e];
+    }
+  }
   __syncthreads();
 
 #pragma unroll

@@ -37,6 +37,9 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 size_t dtype_size(lq_dtype dt) { return dt == LQ_F32 ? 4 : 2; }
 
+// lq_gemm addresses a 128-row or 128-token block with 32-bit buffer offsets
+constexpr int64_t kGemmMaxK = int64_t{1} << 22;
+
 }  // namespace
 
 extern "C" {
@@ -102,9 +105,9 @@ lq_status lq_lift_activations(const void* a, lq_dtype a_dtype, int64_t B, int64_
   if (n % d) return fail(LQ_ERR_SHAPE, "n=%lld not a multiple of d=%d", (long long)n, (int)d);
   if ((int64_t)n / d * D > INT32_MAX || n > INT32_MAX || B > INT32_MAX / 2)
     return fail(LQ_ERR_SHAPE, "sizes exceed 32-bit indexing");
-  if (!aligned(t_inv, 16)) return fail(LQ_ERR_ALIGN, "t_inv must be 16-byte aligned");
-  if (!aligned(a, dtype_size(a_dtype)) || !aligned(a_lift, dtype_size(lift_dtype)) ||
-      !aligned(M, 4))
+  if (!aligned(t_inv, 16) || !aligned(a, 16))
+    return fail(LQ_ERR_ALIGN, "t_inv and a must be 16-byte aligned");
+  if (!aligned(a_lift, dtype_size(lift_dtype)) || !aligned(M, 4))
     return fail(LQ_ERR_ALIGN, "misaligned pointer");
   return hip_status(lq::launch_lift(a, a_dtype, B, n, t_inv, t_dtype, M, d, D, a_lift, lift_dtype,
                                     as_stream(stream)),
@@ -176,8 +179,9 @@ lq_status lq_gemm(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw, c
     return fail(LQ_ERR_SHAPE, "m=%lld K=%lld B=%lld", (long long)m, (long long)K, (long long)B);
   if (ldw < (K + 31) / 32) return fail(LQ_ERR_SHAPE, "ldw=%lld < ceil(K/32)", (long long)ldw);
   if (K % 8) return fail(LQ_ERR_SHAPE, "K=%lld must be a multiple of 8", (long long)K);
-  if (m > INT32_MAX || B > INT32_MAX || K > INT32_MAX)
-    return fail(LQ_ERR_SHAPE, "sizes out of range");
+  if (m > INT32_MAX || B > INT32_MAX || K > kGemmMaxK || ldw > kGemmMaxK)
+    return fail(LQ_ERR_SHAPE, "m=%lld B=%lld must be < 2^31, K=%lld and ldw=%lld <= 2^22",
+                (long long)m, (long long)B, (long long)K, (long long)ldw);
   if (!aligned(w_packed, 4)) return fail(LQ_ERR_ALIGN, "w_packed must be 4-byte aligned");
   if (!aligned(a_lift, 16)) return fail(LQ_ERR_ALIGN, "a_lift must be 16-byte aligned");
   if (!aligned(s, 4) || !aligned(out, 4)) return fail(LQ_ERR_ALIGN, "misaligned s or out");

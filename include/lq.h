@@ -94,7 +94,8 @@ lq_status lq_unpack_signs(const uint32_t* packed, int64_t rows, int64_t K, int64
  * a_lift: [B][K] of lift_dtype, K = n*D/d.  LQ_F32 feeds lq_gemv; LQ_F16 or
  *         LQ_BF16 (round to nearest even) feed lq_gemm.
  * Accumulation is float32.  Requires t_block == 128, n % 128 == 0,
- * n % d == 0, 1 <= d <= 64, 1 <= D <= 256, d*D <= 8192, B >= 1.
+ * n % d == 0, 1 <= d <= 64, 1 <= D <= 256, d*D <= 8192, B >= 1; a and t_inv
+ * 16-byte aligned (16-byte loads), M and a_lift aligned to their element.
  */
 lq_status lq_lift_activations(const void* a, lq_dtype a_dtype, int64_t B, int64_t n,
                               const void* t_inv, lq_dtype t_dtype, int32_t t_block,
@@ -151,8 +152,13 @@ lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw,
  * cores: out[b][i] = s[i] * sum_k sigma_ik * a_lift[b][k] with a_lift in
  * 16-bit (LQ_F16 or LQ_BF16) [B][K]; signs are expanded to exact +-1 16-bit
  * tiles and multiplied with float32 accumulation.
- * w_packed: as for lq_gemv; a_lift 16-byte aligned, K % 8 == 0.
- * out: float [B][m].  Requires B >= 1, m >= 1, K >= 1.
+ * w_packed: uint32 [m][ldw] (layout of lq_pack_signs), ldw >= ceil(K/32),
+ *           4-byte aligned.
+ * a_lift:   16-byte aligned, K % 8 == 0.
+ * out:      float [B][m].
+ * Requires 1 <= B < 2^31, 1 <= m < 2^31, 1 <= K <= 2^22 and ldw <= 2^22;
+ * otherwise LQ_ERR_SHAPE, LQ_ERR_ALIGN or LQ_ERR_DTYPE and nothing is
+ * launched.  Each output is one float32 sum in a fixed order (deterministic).
  */
 lq_status lq_gemm(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw,
                   const float* s, const void* a_lift, lq_dtype lift_dtype, int64_t B,

@@ -93,6 +93,7 @@ def test_lift_validation(L):
     assert call(n=1280, d=64, D=200) == 2   # d*D > 8192
     assert call(B=0) == 2
     assert call(t=MIS) == 4
+    assert call(a=P + 8) == 4         # activations not 16-byte aligned
     assert ok  # the happy path needs a GPU and is covered by the GPU tests
 
 

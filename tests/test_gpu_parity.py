@@ -194,18 +194,28 @@ def test_gemv_one_token_scaling_is_exact(dev):
 
 
 # ----------------------------------------------------------------- GEMM
-GEMM_CASES = [  # (m, K, B)
-    (128, 256, 128), (200, 520, 130), (33, 64, 1), (1000, 2048, 300), (256, 20480, 64),
+GEMM_CASES = [  # (m, K, B, extra words of row stride)
+    (128, 256, 128, 0), (200, 520, 130, 0), (33, 64, 1, 0), (1000, 2048, 300, 0),
+    (256, 20480, 64, 0),
+    (129, 384, 257, 0),    # an odd number of 128-position steps; ragged row and token tiles
+    (70, 40, 5, 0),        # K below one step, odd word stride (ldw = 2)
+    (300, 1000, 200, 3),   # K % 128 != 0, padded rows (ldw = 35)
+    (1030, 4096, 129, 1),  # several row tiles with a ragged tail, one token past a tile
 ]
 
 
 @pytest.mark.parametrize("odt", [torch.float16, torch.bfloat16])
-@pytest.mark.parametrize("m,K,B", GEMM_CASES)
-def test_gemm_lifted_product(dev, m, K, B, odt):
-    _banner(f"gemm m={m} K={K} B={B} {odt}")
+@pytest.mark.parametrize("m,K,B,pad", GEMM_CASES)
+def test_gemm_lifted_product(dev, m, K, B, pad, odt):
+    _banner(f"gemm m={m} K={K} B={B} pad={pad} {odt}")
     rng = np.random.default_rng(m + K + B)
-    ldw = (K + 31) // 32
+    ldw = (K + 31) // 32 + pad
     packed = synth.random_sign_words(rng, m, K, ldw=ldw)
+    # bits past K and padding words hold garbage that must not reach the sums
+    tail = rng.integers(0, 2**32, size=(m, ldw - K // 32), dtype=np.uint64).astype(np.uint32)
+    if K % 32:
+        tail[:, 0] &= np.uint32(~((1 << (K % 32)) - 1) & 0xFFFFFFFF)
+    packed[:, K // 32:] |= tail
     al = torch.from_numpy(rng.standard_normal((B, K)).astype(np.float32)).to(odt)
     s = rng.uniform(0.01, 0.03, m).astype(np.float32)
     # the oracle sees exactly the stored 16-bit activations
