@@ -47,8 +47,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--gemm-dtype", default="f16", choices=["f16", "bf16"])
     p.add_argument("--no-cases", action="store_true", help="skip the per-workload sweep")
-    p.add_argument("--only", default="all", choices=["all", "layer", "gemm"],
-                   help="layer: only the timed 70B steps; gemm: only the batch-512 GEMM")
+    p.add_argument("--only", default="all", choices=["all", "layer", "gemm", "cases"],
+                   help="layer: only the timed 70B steps; gemm: only the batch-512 GEMM; "
+                        "cases: only the per-workload GEMV and lift sweep")
     return p.parse_args()
 
 
@@ -124,6 +125,8 @@ def run_gpu(args):
     lq.load_library()
     if args.only == "gemm":
         return dict(gemm=run_gemm(args, torch, lq, synth, dev))
+    if args.only == "cases":
+        return dict(cases=run_cases(torch, lq, synth, dev))
     cfg = synth.CONFIGS[3]                     # LQ-19/8 70B-class MLP
     layers = [synth.make_case(cfg, si, 1) for si in range(len(cfg.shapes))]
     rots = [Rotation(L, torch, lq, dev) for L in layers]
@@ -219,6 +222,14 @@ def capture_graphs(torch, fns):
     return graphs
 
 
+def graph_time(torch, fn, R, n_rep, st):
+    """Average duration of one fn(k) launch: a HIP graph of fn(0) .. fn(R - 1)
+    back to back, replayed n_rep times between HIP events on st, so the host's
+    launch rate does not enter."""
+    g = capture_graphs(torch, [lambda: [fn(k) for k in range(R)]])[0]
+    return time_launches(torch, lambda i: g.replay(), n_rep, st) / R
+
+
 def time_launches(torch, fn, n, st):
     """Average duration of fn() over n back-to-back calls, HIP events on st."""
     e0 = torch.cuda.Event(enable_timing=True)
@@ -245,11 +256,11 @@ def run_gemm(args, torch, lq, synth, dev):
         lq.lift(rot.a, c.t_inv, c.M, L.d, L.D, out=als[i % 2])
         lq.gemm(c.w, c.s, als[i % 2], L.K, out=out)
     torch.cuda.synchronize()
-    n = max(5, min(args.steps, 40))
-    lift_ms = time_launches(torch, lambda i: lq.lift(rot.a, rot[i].t_inv, rot[i].M, L.d, L.D,
-                                                     out=als[i % 2]), n, st)
-    gemm_ms = time_launches(torch, lambda i: lq.gemm(rot[i].w, rot[i].s, als[i % 2], L.K, out=out),
-                            n, st)
+    n = max(3, min(args.steps, 20))
+    lift_ms = graph_time(torch, lambda k: lq.lift(rot.a, rot[k].t_inv, rot[k].M, L.d, L.D,
+                                                  out=als[k % 2]), rot.R, n, st)
+    gemm_ms = graph_time(torch, lambda k: lq.gemm(rot[k].w, rot[k].s, als[k % 2], L.K, out=out),
+                         rot.R, n, st)
     flops = 2.0 * L.m * L.K * L.B
     tf = flops / (gemm_ms * 1e-3) / 1e12
     return {"workload": f"LQ-40/16 {L.m}x{L.n} batch {L.B}, lifted K={L.K}",
@@ -263,7 +274,8 @@ def run_gemm(args, torch, lq, synth, dev):
 
 
 def run_cases(torch, lq, synth, dev):
-    """GEMV (B <= 16) per workload case: back-to-back launches on rotating copies."""
+    """GEMV (B <= 16) per workload case: graphs of back-to-back launches on
+    rotating copies."""
     res = []
     st = torch.cuda.current_stream()
     for cfg, si, (m, n), B in synth.all_cases():
@@ -277,9 +289,9 @@ def run_cases(torch, lq, synth, dev):
         for i in range(3):
             lq.gemv(rot[i].w, rot[i].s, al, L.K, out=out)
         torch.cuda.synchronize()
-        g = time_launches(torch, lambda i: lq.gemv(rot[i].w, rot[i].s, al, L.K, out=out), 30, st)
-        lt = time_launches(torch, lambda i: lq.lift(rot.a, rot[i].t_inv, rot[i].M, L.d, L.D,
-                                                    out=al), 30, st)
+        g = graph_time(torch, lambda k: lq.gemv(rot[k].w, rot[k].s, al, L.K, out=out), rot.R, 10, st)
+        lt = graph_time(torch, lambda k: lq.lift(rot.a, rot[k].t_inv, rot[k].M, L.d, L.D, out=al),
+                        rot.R, 10, st)
         gb = gemv_bytes(m, L.K, B) / (g * 1e-3) / 1e9
         res.append({"case": f"{cfg.name} {m}x{n} B={B}", "gemv_us": round(g * 1e3, 2),
                     "gemv_GBs": round(gb, 1), "gemv_frac": round(gb / HBM_PEAK_GBS, 3),
@@ -339,11 +351,11 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
-              f"(this path is single-GPU; see the sharding notes in DESIGN.md)", file=sys.stderr)
+              f"(the path runs on one GPU; sharding over several is not built)", file=sys.stderr)
         sys.exit(2)
     r = run_gpu(args)
-    if args.only == "gemm":
-        print(json.dumps({"gemm": r["gemm"]}), flush=True)
+    if args.only in ("gemm", "cases"):
+        print(json.dumps({args.only: r[args.only]}), flush=True)
         return
     cpu = None if args.no_cpu else cpu_baseline(r["layers"], r["outs"], args.cpu_seconds)
     line = {

@@ -92,15 +92,28 @@ struct Mfma<LQ_BF16> {
   }
 };
 
+// Values the compiler cannot fold (no instruction is emitted for them): a
+// scalar, and a per-lane value (kept in a vector register).
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+__device__ __forceinline__ uint32_t opaque_v(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+// (x & mask) | one for a mask that `one` does not touch, written as a
+// bitfield insert so that it is one v_bfi_b32 that the compiler schedules
+// (and spaces from the MFMA that reads it) like any other instruction.
 __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t one) {
-  uint32_t d;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(x), "s"(mask), "v"(one));
-  return d;
+  return (x & mask) | (one & ~mask);
 }
 
 // Byte `byte_idx` of `word` -> 8 16-bit values -sigma (bit 1 -> -1, bit 0 -> +1).
 template <int DT>
-__device__ __forceinline__ uint4 expand_byte(uint32_t word, int byte_idx, uint32_t one) {
+__device__ __forceinline__ uint4 expand_byte(uint32_t word, int byte_idx, uint32_t sgn,
+                                             uint32_t one) {
   const uint32_t selr = static_cast<uint32_t>(byte_idx) | 0x0C000C00u |
                         (static_cast<uint32_t>(byte_idx) << 16);
   const uint32_t rep = __builtin_amdgcn_perm(0u, word, selr);   // [x, 0, x, 0]
@@ -113,7 +126,7 @@ __device__ __forceinline__ uint4 expand_byte(uint32_t word, int byte_idx, uint32
     const us2 h = r << sh;
     uint32_t hv;
     __builtin_memcpy(&hv, &h, 4);
-    d[p] = and_or(hv, 0x80008000u, one);
+    d[p] = and_or(hv, sgn, one);
   }
   return make_uint4(d[0], d[1], d[2], d[3]);
 }
@@ -206,7 +219,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(
     for (int nj = 0; nj < 4; ++nj)
       bf[nj] = *reinterpret_cast<const uint4*>(b_frag + buf * kBufElems + nj * 32 * kLdsRow + 8 * c);
   };
-  const uint32_t one = Mfma<DT>::kOneOne;
+  const uint32_t one = opaque_v(Mfma<DT>::kOneOne);
+  const uint32_t sgn = opaque(0x80008000u);
 
   const int steps = (K + kKS - 1) / kKS;
   uint32_t a[kRing][2];
@@ -233,7 +247,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(
     uint4 af[2], afn[2];
     read_b(buf, 0, bf);
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) af[mi] = expand_byte<DT>(a[p][mi], 0, one);
+    for (int mi = 0; mi < 2; ++mi) af[mi] = expand_byte<DT>(a[p][mi], 0, sgn, one);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -243,7 +257,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_mfma_kernel(
       }
       if (c < 3) {
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) afn[mi] = expand_byte<DT>(a[p][mi], c + 1, one);
+        for (int mi = 0; mi < 2; ++mi) afn[mi] = expand_byte<DT>(a[p][mi], c + 1, sgn, one);
       }
       // token block nj's fragment is reloaded for sub-step c + 1 as soon as
       // its two MFMAs of sub-step c are issued

@@ -34,10 +34,46 @@
 // the critical path; the kernel boundary costs less than that.
 #include <type_traits>
 
-#include "lut_common.h"
+#include "lq_internal.h"
 
 namespace lq {
 namespace {
+
+constexpr int kSliceBits = 1024;                // lifted positions per table
+constexpr int kSliceBytes = kSliceBits / 8;     // 128
+constexpr uint32_t kNoLoad = 0x80000000u;       // outside every buffer resource: loads give 0
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int o = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false);
+  return v + __int_as_float(o);
+}
+
+// Sum over the 8 lanes of an aligned lane group; every lane gets the total.
+__device__ __forceinline__ float sum8(float v) {
+  v = dpp_add<0xB1>(v);    // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]
+  v = dpp_add<0x141>(v);   // row_half_mirror
+  return v;
+}
+
+__host__ __device__ constexpr int gray(int i) { return i ^ (i >> 1); }
+__host__ __device__ constexpr int ctz6(int i) {
+  return (i & 1) ? 0 : (i & 2) ? 1 : (i & 4) ? 2 : (i & 8) ? 3 : (i & 16) ? 4 : 5;
+}
+
+// Activations of byte position p of slice sl for token t (zero past K).
+__device__ __forceinline__ void load_x(__amdgpu_buffer_rsrc_t ares, int64_t K, int t, int sl,
+                                       int p, float4& x0, float4& x1) {
+  const int64_t k0 = (int64_t)sl * kSliceBits + 8 * p;
+  const uint32_t base = static_cast<uint32_t>(((int64_t)t * K + k0) * 4);
+  const uint32_t o0 = (k0 + 4 <= K) ? base : kNoLoad;
+  const uint32_t o1 = (k0 + 8 <= K) ? base + 16 : kNoLoad;
+  const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(ares, o0, 0, 0);
+  const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(ares, o1, 0, 0);
+  __builtin_memcpy(&x0, &v0, 16);
+  __builtin_memcpy(&x1, &v1, 16);
+}
 
 #ifndef LQ_GEMV1_WAVES
 #define LQ_GEMV1_WAVES 16
@@ -468,9 +504,8 @@ Sched1 make_sched1(int64_t m, int64_t K) {
 size_t gemv1_workspace_bytes(int64_t m, int64_t K) {
   const Sched1 sc = make_sched1(m, K);
   if (sc.S == 1) return 0;
-  // partial sums after the counter region of the several-token kernel, which
-  // must stay zero
-  return gemv_counter_bytes(m) + sizeof(float) * kGranuleRows * (size_t)sc.NG * sc.S;
+  // one partial sum per (granule row, slice); every one is written each call
+  return sizeof(float) * kGranuleRows * (size_t)sc.NG * sc.S;
 }
 
 hipError_t launch_gemv1(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
@@ -482,7 +517,7 @@ hipError_t launch_gemv1(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, co
     hipLaunchKernelGGL(gemv1_kernel<false>, dim3(sc.G), dim3(kThreads), 0, st, w, m, K, ldw, s,
                        a_lift, out, nullptr, sc, w_bytes, a_bytes);
   } else {
-    float* partials = reinterpret_cast<float*>(static_cast<char*>(ws) + gemv_counter_bytes(m));
+    float* partials = static_cast<float*>(ws);
     hipLaunchKernelGGL(gemv1_kernel<true>, dim3(sc.G), dim3(kThreads), 0, st, w, m, K, ldw, s,
                        a_lift, out, partials, sc, w_bytes, a_bytes);
     const hipError_t e = hipGetLastError();

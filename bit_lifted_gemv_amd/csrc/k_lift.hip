@@ -222,6 +222,8 @@ hipError_t dispatch_t(const void* a, int64_t B, int64_t n, const void* t_inv, lq
 hipError_t launch_lift(const void* a, lq_dtype a_dt, int64_t B, int64_t n, const void* t_inv,
                        lq_dtype t_dt, const float* M, int d, int D, void* out, lq_dtype out_dt,
                        hipStream_t st) {
+  if (lift_mfma_applies(a_dt, t_dt, B, n, d, D))
+    return launch_lift_mfma(a, a_dt, B, n, t_inv, M, d, D, out, out_dt, st);
   switch (a_dt) {
     case LQ_F32: return dispatch_t<LQ_F32>(a, B, n, t_inv, t_dt, M, d, D, out, out_dt, st);
     case LQ_F16: return dispatch_t<LQ_F16>(a, B, n, t_inv, t_dt, M, d, D, out, out_dt, st);

@@ -118,7 +118,7 @@ lq_status lq_gemv_workspace_size(int64_t m, int64_t K, int64_t B, size_t* bytes)
   if (!bytes) return fail(LQ_ERR_NULL, "bytes is null");
   if (m < 1 || K < 1 || B < 1 || B > 16)
     return fail(LQ_ERR_SHAPE, "m=%lld K=%lld B=%lld", (long long)m, (long long)K, (long long)B);
-  *bytes = B == 1 ? lq::gemv1_workspace_bytes(m, K) : lq::gemv_workspace_bytes(m, K, B);
+  *bytes = B == 1 ? lq::gemv1_workspace_bytes(m, K) : lq::gemv_mfma_workspace_bytes(m, K, B);
   return ok();
 }
 
@@ -148,7 +148,7 @@ lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw, c
   if (!aligned(w_packed, 16)) return fail(LQ_ERR_ALIGN, "w_packed must be 16-byte aligned");
   if (!aligned(a_lift, 16)) return fail(LQ_ERR_ALIGN, "a_lift must be 16-byte aligned");
   if (!aligned(s, 4) || !aligned(out, 4)) return fail(LQ_ERR_ALIGN, "misaligned s or out");
-  const size_t need = B == 1 ? lq::gemv1_workspace_bytes(m, K) : lq::gemv_workspace_bytes(m, K, B);
+  const size_t need = B == 1 ? lq::gemv1_workspace_bytes(m, K) : lq::gemv_mfma_workspace_bytes(m, K, B);
   if (need > 0) {
     if (!workspace) return fail(LQ_ERR_WORKSPACE, "workspace of %zu bytes required", need);
     if (workspace_bytes < need)
@@ -159,15 +159,9 @@ lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw, c
     return hip_status(lq::launch_gemv1(w_packed, m, K, ldw, s, a_lift, out, workspace,
                                        as_stream(stream)),
                       "lq_gemv launch");
-  // Tokens go through in groups of at most 4; each group rereads the weights.
-  for (int64_t t0 = 0; t0 < B; t0 += 4) {
-    const int64_t bt = (B - t0) < 4 ? (B - t0) : 4;
-    const lq::GemvPlan pl = lq::plan_gemv(m, K, bt);
-    const hipError_t e = lq::launch_gemv(pl, w_packed, m, K, ldw, s, a_lift + t0 * K, bt,
-                                         out + t0 * m, workspace, as_stream(stream));
-    if (e != hipSuccess) return hip_status(e, "lq_gemv launch");
-  }
-  return ok();
+  return hip_status(lq::launch_gemv_mfma(w_packed, m, K, ldw, s, a_lift, B, out, workspace,
+                                         as_stream(stream)),
+                    "lq_gemv launch");
 }
 
 lq_status lq_gemm(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw, const float* s,

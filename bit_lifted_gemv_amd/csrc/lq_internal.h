@@ -79,30 +79,26 @@ hipError_t launch_lift(const void* a, lq_dtype a_dt, int64_t B, int64_t n, const
                        lq_dtype t_dt, const float* M, int d, int D, void* out, lq_dtype out_dt,
                        hipStream_t st);
 
+// The matrix-core lift (k_lift_mfma.hip) takes over from this many tokens
+// when a and T^-1 share a 16-bit type and d divides 128 (d = 4, 8, 16, 32).
+constexpr int64_t kLiftMfmaMinTokens = 17;
+bool lift_mfma_applies(lq_dtype a_dt, lq_dtype t_dt, int64_t B, int64_t n, int d, int D);
+hipError_t launch_lift_mfma(const void* a, lq_dtype dt, int64_t B, int64_t n, const void* t_inv,
+                            const float* M, int d, int D, void* out, lq_dtype out_dt,
+                            hipStream_t st);
+
 // Compute units of the current device (cached per device).
 int num_cus();
 
-// GEMV plan: how the rows and the lifted dimension are split over workgroups.
-struct GemvPlan {
-  int rows_per_wg;      // multiple of 64
-  int slices_per_part;  // 512-bit slices handled by one workgroup
-  int parts;            // number of K-parts (split-K factor)
-  int row_blocks;
-  int slices;           // ceil(K / 512)
-  size_t ws_bytes;      // partial sums + arrival counters (0 when parts == 1)
-};
-GemvPlan plan_gemv(int64_t m, int64_t K, int64_t B);
-size_t gemv_counter_bytes(int64_t m);
-// Workspace bytes of lq_gemv for B tokens (they go through in groups of <= 4).
-size_t gemv_workspace_bytes(int64_t m, int64_t K, int64_t B);
-hipError_t launch_gemv(const GemvPlan& plan, const uint32_t* w, int64_t m, int64_t K,
-                       int64_t ldw, const float* s, const float* a_lift, int64_t B, float* out,
-                       void* ws, hipStream_t st);
-
-// One-token GEMV (lq_gemv with B == 1).
+// One-token GEMV on float16 activation-sum tables (k_gemv1.hip).
 size_t gemv1_workspace_bytes(int64_t m, int64_t K);
 hipError_t launch_gemv1(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
                         const float* a_lift, float* out, void* ws, hipStream_t st);
+
+// Few-token GEMV on the matrix cores (k_gemv_mfma.hip), 1 <= B <= 16.
+size_t gemv_mfma_workspace_bytes(int64_t m, int64_t K, int64_t B);
+hipError_t launch_gemv_mfma(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
+                            const float* a_lift, int64_t B, float* out, void* ws, hipStream_t st);
 
 hipError_t launch_gemm(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
                        const void* a_lift, lq_dtype dt, int64_t B, float* out, hipStream_t st);

@@ -147,13 +147,12 @@ _WS = {}
 
 
 def workspace(nbytes: int, device: torch.device, m: int = 0) -> torch.Tensor:
-    """A zeroed GEMV workspace of at least nbytes for row count m, cached per
-    (device, m) and grown on demand: the library keeps the arrival counters at
-    its head zero between calls with the same m, not across row counts."""
+    """A GEMV workspace of at least nbytes, cached per (device, m) and grown
+    on demand (its contents need no initialisation)."""
     key = (device.type, device.index, m)
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _WS[key] = ws
     return ws
 

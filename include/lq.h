@@ -110,11 +110,8 @@ lq_status lq_gemv_workspace_size(int64_t m, int64_t K, int64_t B, size_t* bytes)
 
 /*
  * lq_workspace_clear -- zero `bytes` bytes of a workspace on `stream` with a
- * fill kernel.  A workspace must be cleared before its first use with a given
- * row count m: its head holds arrival counters that must read zero, and every
- * completed lq_gemv call with that m (any K, any B) leaves them zero again.
- * A call with another m may find partial sums of an earlier call where its
- * counters go: clear the workspace first, or keep one workspace per m.
+ * fill kernel.  lq_gemv needs no cleared workspace (every call writes what it
+ * reads back); this is a convenience for callers that want a known state.
  */
 lq_status lq_workspace_clear(void* workspace, size_t bytes, void* stream);
 
@@ -122,8 +119,7 @@ lq_status lq_workspace_clear(void* workspace, size_t bytes, void* stream);
  * lq_gemv -- the product of the 1-bit weights with the float lifted
  * activations for small batches (关键设计 4 calls this the main body: an
  * ordinary GEMM between 1-bit weights and floats, with no weight codebook to
- * look up).  The kernel does keep lookup tables, but of activation sums built
- * per call from a_lift, not of weights:
+ * look up):
  *   out[b][i] = s[i] * sum_{k<K} sigma_ik * a_lift[b][k],
  *   sigma_ik = +1 if bit k of row i is 1, else -1.
  * w_packed: uint32 [m][ldw] (layout of lq_pack_signs), ldw >= ceil(K/32),
@@ -132,16 +128,21 @@ lq_status lq_workspace_clear(void* workspace, size_t bytes, void* stream);
  * a_lift:   float [B][K] (lq_lift_activations with LQ_F32), 16-byte aligned,
  *           K % 4 == 0.
  * out:      float [B][m].
- * workspace: device buffer of >= lq_gemv_workspace_size bytes, cleared once
- *           (lq_workspace_clear); may be NULL when that size is 0.
+ * workspace: device buffer of >= lq_gemv_workspace_size bytes, 256-byte
+ *           aligned, owned by the caller; may be NULL when that size is 0.
+ *           Its contents need no initialisation.  Calls that share a
+ *           workspace must not overlap.
  * Requires 1 <= B <= 16, m >= 1, K >= 1, m*ldw*4 <= 2^30 bytes (split
  * larger matrices by rows over several calls) and K <= 2^24.  Accumulation
  * is float32 and the result does not depend on timing (partial sums over the
- * lifted dimension are added in a fixed order, no float atomics).  With
- * B >= 2 the activation-sum tables are float32; with B == 1 they are float16,
- * each slice's activations scaled by an exact power of two first, so every
- * table entry carries one float16 rounding (relative 2^-11) whatever the
- * range of a_lift: a relative output error of about 3e-4.
+ * lifted dimension are added in a fixed order, no float atomics).
+ * Arithmetic: with B == 1 the kernel keeps tables of activation sums (not
+ * of weights) in float16, each slice's activations scaled by an exact power
+ * of two first, so every table entry carries one float16 rounding (relative
+ * 2^-11) whatever the range of a_lift: a relative output error of about
+ * 3e-4.  With B >= 2 the product runs on the matrix cores: each activation
+ * is split into two bfloat16 parts (hi + lo, relative error below 2^-17)
+ * and multiplied by exact +-1 signs.
  */
 lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw,
                   const float* s, const float* a_lift, int64_t B, float* out,

@@ -21,9 +21,11 @@ from oracle import lq_oracle as O
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
-# With B >= 2 the GEMV adds float32 activation sums in float32 (about K/8 + 8
-# roundings per output on top of the float32 lifted operand): 1e-4 bounds it
-# with a wide margin at every K here.
+# With B >= 2 the GEMV splits each float32 activation into two bfloat16 parts
+# (hi + lo carry 16 significant bits: relative error <= 2^-17 per value,
+# independent across the K values of a row) and multiplies them by exact +-1
+# on the matrix cores with float32 accumulation (about K/32 roundings of the
+# running sum): 1e-4 bounds both with a wide margin at every K here.
 TOL_F32 = 1e-4
 # With B == 1 each activation sum (8 terms) is rounded once to float16 after
 # an exact power-of-two scaling: relative error <= 2^-11 per table entry,
@@ -75,6 +77,10 @@ LIFT_CASES = [  # (n, d, D, B, act dtype)
     (512, 8, 20, 16, "bf16"), (256, 16, 40, 33, "bf16"), (384, 8, 16, 4, "f16"),
     (384, 3, 7, 2, "bf16"), (256, 64, 128, 1, "f16"), (1280, 40, 100, 2, "bf16"),
     (640, 32, 80, 20, "f16"),
+    # 17 tokens and more with a and T^-1 of one 16-bit type and d | 128 take
+    # the matrix-core lift: ragged token tiles, D % 8 != 0, d = 4 .. 32
+    (1024, 8, 19, 130, "bf16"), (512, 4, 9, 17, "f16"), (384, 16, 40, 257, "f16"),
+    (2048, 8, 20, 64, "bf16"), (256, 32, 64, 40, "bf16"),
 ]
 
 
@@ -90,8 +96,8 @@ def test_lift_float32(dev, n, d, D, B, dt):
 
 
 @pytest.mark.parametrize("odt", [torch.float16, torch.bfloat16])
-def test_lift_16bit_outputs(dev, odt):
-    n, d, D, B = 1024, 8, 19, 5
+@pytest.mark.parametrize("n,d,D,B", [(1024, 8, 19, 5), (1024, 8, 19, 70), (512, 16, 40, 300)])
+def test_lift_16bit_outputs(dev, odt, n, d, D, B):
     L = synth.make_layer(4, n, d, D, B, seed=3, dtype="bf16")
     ref = O.lift(O.transform(O.decode(L.a, "bf16"), O.decode(L.t_inv, "bf16")), L.M, d, D)
     got = lq.lift(_up(L.a, "bf16", dev), _up(L.t_inv, "bf16", dev),
@@ -140,7 +146,7 @@ def test_gemv_deterministic(dev):
 
 def test_gemv_token_counts_share_a_workspace(dev):
     """Calls with one m and different B (different kernels and splits) run on
-    one workspace: each leaves the arrival counters zero for the next."""
+    one workspace, each over what the previous call left in it."""
     _banner("gemv B = 1, 4, 1, 2, 1 on one workspace")
     rng = np.random.default_rng(5)
     m, K = 2050, 12288
