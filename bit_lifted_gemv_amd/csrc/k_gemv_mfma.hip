@@ -28,7 +28,8 @@
 // Kernels.  A small preparation kernel writes the bfloat16 parts once, in
 // the order the MFMA B operand is read (per word-block and tile, 64 lanes x
 // 16 bytes), to the workspace.  The main kernel gives each wave RT tiles of
-// 16 rows; a workgroup of 8 waves (two per SIMD) shares the activation parts
+// 16 rows; a workgroup of 8 waves (two per SIMD) shares the
+// activation parts
 // of 16 word-blocks at a time in LDS (double-buffered; each chunk is loaded
 // into registers two chunks ahead and written to LDS one chunk ahead) and
 // streams its weights from HBM, 16 bytes (4 words) per lane, tile and span,
@@ -48,10 +49,9 @@ typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;                 // two per SIMD
-constexpr int kThreads = 64 * kWaves;
 constexpr uint32_t kOneOne = 0x3F803F80u;  // bfloat16 (+1, +1)
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
+constexpr uint32_t kFar = 0x40000000u;     // past every weight range (<= 2^30 bytes)
 
 // Values the compiler cannot fold (no instruction is emitted for them): a
 // scalar, and a per-lane value (kept in a vector register).
@@ -124,14 +124,15 @@ __global__ void __launch_bounds__(256) gemv_mfma_prep_kernel(const float* __rest
 }
 
 // RT: 16-row tiles per wave; NB: 16-column tiles (8 tokens each); kCB:
-// word-blocks (32 positions each) per chunk.
+// MFMA steps (32 positions each) per chunk; kW: waves per workgroup.
 // Grid: x = row groups of 4 waves, y = splits of the lifted dimension (whole
 // chunks each).  partials == nullptr: write s-scaled sums to out.
-template <int RT, int NB, int kCB>
-__global__ void __launch_bounds__(kThreads, 1) gemv_mfma_kernel(
-    const uint32_t* __restrict__ w, int m, int ldw, const float* __restrict__ s,
+template <int RT, int NB, int kCB, int kW>
+__global__ void __launch_bounds__(64 * kW, 1) gemv_mfma_kernel(
+    const uint32_t* __restrict__ w, int m, int ldw, int nw, const float* __restrict__ s,
     const uint4* __restrict__ bws, int B, int nchunks, float* __restrict__ out,
     float* __restrict__ partials) {
+  constexpr int kThreads = 64 * kW;
   __shared__ u32x4 sb[2][kCB * NB * 64];     // 2 kCB KB per tile of columns
 
   const int tid = threadIdx.x;
@@ -147,8 +148,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_mfma_kernel(
   // Weights of this workgroup's rows; rows past m read as zero.  Words past
   // a row's end (the last chunk may reach past ldw) pair with zero
   // activations.  Offsets stay below 2^31 (m * ldw * 4 <= 2^30).
-  const int wg_row0 = blockIdx.x * kWaves * 16 * RT;
-  const int wg_rows = min(kWaves * 16 * RT, m - wg_row0);
+  const int wg_row0 = blockIdx.x * kW * 16 * RT;
+  const int wg_rows = min(kW * 16 * RT, m - wg_row0);
   const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(w + static_cast<int64_t>(wg_row0) * ldw), (short)0,
       static_cast<int>(static_cast<uint32_t>(wg_rows) * static_cast<uint32_t>(ldw) * 4u), kRsrcWord3);
@@ -159,9 +160,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_mfma_kernel(
   // weights of chunk c, span q (16 words), tile t: lane (i, g) takes words
   // 4 g .. 4 g + 3 of the span of row i, so one load covers 64 contiguous
   // bytes of each of the tile's 16 rows
+  // Spans past this split (a scalar choice) or words past the row's last
+  // one, nw (a per-lane choice), are not fetched: their offsets fall outside
+  // the range (each part is 2^30 or more and the range is at most 2^30
+  // bytes, the sum stays below 2^32) and read as zero.
   auto load_w = [&](int c, int q, int t) -> uint4 {
-    const auto r = __builtin_amdgcn_raw_buffer_load_b128(wres, w_off[t],
-                                                         (c * kCB + 16 * q) * 4, 0);
+    const int word0 = c * kCB + 16 * q + 4 * g;
+    const uint32_t vo = word0 < nw ? w_off[t] : kFar;
+    const int so = c < c1 ? (c * kCB + 16 * q) * 4 : static_cast<int>(kFar);
+    const auto r = __builtin_amdgcn_raw_buffer_load_b128(wres, vo, so, 0);
     uint4 v;
     __builtin_memcpy(&v, &r, 16);
     return v;
@@ -300,25 +307,27 @@ __global__ void __launch_bounds__(256) gemv_mfma_reduce_kernel(const float* __re
 }
 
 struct Plan {
-  int RT, NB, CB, S, nblk, nchunks;
+  int RT, NB, CB, W, S, nblk, nchunks;
   size_t b_bytes, p_bytes;
 };
 
 Plan plan(int64_t m, int64_t K, int64_t B) {
   Plan p;
   p.NB = B <= 8 ? 1 : 2;
-  p.RT = p.NB == 1 ? 2 : 4;
-  p.CB = p.NB == 1 ? 32 : 16;
+  p.RT = 4;                                  // 64 rows per wave
+  p.CB = 16;                                 // one span per chunk
+  p.W = 8;                                   // waves per workgroup (2 per SIMD)
   const int kCB = p.CB;
   // an even number of chunks (a padding chunk of zero activations, if
   // needed, adds nothing)
   const int64_t nblk = (K + 31) / 32;
   p.nchunks = static_cast<int>((nblk + 2 * kCB - 1) / (2 * kCB) * 2);
   p.nblk = p.nchunks * kCB;
-  const int64_t waves = (m + 16 * p.RT - 1) / (16 * p.RT);
-  // enough splits of the lifted dimension for about two waves per SIMD
-  const int64_t slots = 8 * static_cast<int64_t>(num_cus());
-  int64_t S = (slots + waves / 2) / waves;
+  // as many splits of the lifted dimension as keep every workgroup on a CU
+  // of its own (no CU runs two of them, which would double its time)
+  const int64_t groups = (m + 16 * p.RT * p.W - 1) / (16 * p.RT * p.W);
+  const int64_t cus = num_cus();
+  int64_t S = cus / groups;
   S = S < 1 ? 1 : S;
   S = S > p.nchunks / 2 ? p.nchunks / 2 : S;
   p.S = static_cast<int>(S);
@@ -328,14 +337,15 @@ Plan plan(int64_t m, int64_t K, int64_t B) {
   return p;
 }
 
-template <int RT, int NB, int CB>
-void launch_main(const Plan& p, const uint32_t* w, int64_t m, int64_t ldw, const float* s,
-                 const uint4* bws, int64_t B, float* out, float* partials, hipStream_t st) {
-  const int rows_wg = kWaves * 16 * RT;
+template <int RT, int NB, int CB, int W>
+void launch_main(const Plan& p, const uint32_t* w, int64_t m, int64_t K, int64_t ldw,
+                 const float* s, const uint4* bws, int64_t B, float* out, float* partials,
+                 hipStream_t st) {
+  const int rows_wg = W * 16 * RT;
   const dim3 grid(static_cast<unsigned>((m + rows_wg - 1) / rows_wg), static_cast<unsigned>(p.S));
-  hipLaunchKernelGGL((gemv_mfma_kernel<RT, NB, CB>), grid, dim3(kThreads), 0, st, w,
-                     static_cast<int>(m), static_cast<int>(ldw), s, bws, static_cast<int>(B),
-                     p.nchunks, out, partials);
+  hipLaunchKernelGGL((gemv_mfma_kernel<RT, NB, CB, W>), grid, dim3(64 * W), 0, st, w,
+                     static_cast<int>(m), static_cast<int>(ldw), static_cast<int>((K + 31) / 32),
+                     s, bws, static_cast<int>(B), p.nchunks, out, partials);
 }
 
 }  // namespace
@@ -355,9 +365,9 @@ hipError_t launch_gemv_mfma(const uint32_t* w, int64_t m, int64_t K, int64_t ldw
   hipLaunchKernelGGL(gemv_mfma_prep_kernel, dim3((prep_threads + 255) / 256), dim3(256), 0, st,
                      a_lift, static_cast<int>(B), static_cast<int>(K), p.NB, p.nblk, bws);
   if (p.NB == 1)
-    launch_main<2, 1, 32>(p, w, m, ldw, s, bws, B, out, partials, st);
+    launch_main<4, 1, 16, 8>(p, w, m, K, ldw, s, bws, B, out, partials, st);
   else
-    launch_main<4, 2, 16>(p, w, m, ldw, s, bws, B, out, partials, st);
+    launch_main<4, 2, 16, 8>(p, w, m, K, ldw, s, bws, B, out, partials, st);
   if (p.S > 1) {
     const int64_t n = B * m;
     hipLaunchKernelGGL(gemv_mfma_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
