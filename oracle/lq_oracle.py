@@ -19,8 +19,9 @@ Readings where the notes are silent (each is also listed with the design
 notes of the repository):
   * "M T^-1 a" does not type-check as written (M is d x D); it is read as
     u = T^-1 a followed by the per-group lift a_hat_g = M^T u_g.
-  * T^-1 is block-diagonal with square blocks (the notes' Kronecker form is a
-    later extension); block q maps a[tb*q + c] to u[tb*q + r] by T_q[r][c].
+  * T^-1 is block-diagonal with square blocks; block q maps a[tb*q + c] to
+    u[tb*q + r] by T_q[r][c].  The notes' Kronecker form of the whitening
+    (关键设计 3) is the second transform below (transform_kron).
   * the lifted index of sign j of group g is k = g*D + j; bit (k & 31) of
     word (k >> 5) of a row is 1 iff the sign is +1.
   * s is a per-output-row scale applied after the contraction.
@@ -34,7 +35,7 @@ import numpy as np
 __all__ = [
     "decode", "unpack_bits", "signs_from_packed", "pack_signs_ref", "reconstruct_weights",
     "transform", "lift", "lifted_product", "forward", "forward_lifted", "forward_loops",
-    "rel_err_colmax",
+    "rel_err_colmax", "kron_inverse_dense", "transform_kron", "lift_kron", "forward_kron",
 ]
 
 
@@ -108,6 +109,75 @@ def lift(u: np.ndarray, M: np.ndarray, d: int, D: int) -> np.ndarray:
     G = n // d
     Mf = M.astype(np.float64)
     return (u.reshape(B, G, d) @ Mf).reshape(B, G * D)
+
+
+# ------------------------------------------------------------------ Kronecker whitening
+# 关键设计 3 writes the per-layer whitening as T = diag(s1) (P1 (x) P2) diag(s2),
+# P1 and P2 small square matrices, s1 a per-channel scale and s2 a scale that
+# is constant over each lift group (so that it folds into M).  The layer
+# applies T^-1 = diag(s2)^-1 (P1 (x) P2)^-1 diag(s1)^-1, and
+# (P1 (x) P2)^-1 = P1^-1 (x) P2^-1.  Readings: the pages' sqrt(n) x sqrt(n)
+# factors are read as n1 x n1 and n2 x n2 with n = n1 n2 (n = 8192 has no
+# integer square root); channel c of a is entry (c // n2, c % n2) of the
+# n1 x n2 reshape (numpy's row-major order, which is the order np.kron
+# uses); the inverses P1^-1, P2^-1 are inputs, as T^-1 is for the
+# block-diagonal form; s2 is given per d-wide lift group.
+
+def kron_inverse_dense(s1: np.ndarray, p1_inv: np.ndarray, p2_inv: np.ndarray,
+                       s2_group: np.ndarray, d: int) -> np.ndarray:
+    """The n x n matrix T^-1 = diag(1/s2) (P1^-1 (x) P2^-1) diag(1/s1), formed
+    densely with np.kron (small n only)."""
+    s1 = np.asarray(s1, dtype=np.float64)
+    s2 = np.repeat(np.asarray(s2_group, dtype=np.float64), d)
+    K = np.kron(np.asarray(p1_inv, dtype=np.float64), np.asarray(p2_inv, dtype=np.float64))
+    return (K / s2[:, None]) / s1[None, :]
+
+
+def transform_kron(a: np.ndarray, s1: np.ndarray, p1_inv: np.ndarray, p2_inv: np.ndarray,
+                   s2_group: np.ndarray, d: int, dense: Optional[bool] = None) -> np.ndarray:
+    """u = T^-1 a for the Kronecker form, a [B][n] float64.  dense=True applies
+    the dense matrix of kron_inverse_dense; dense=False uses, per token, the
+    n1 x n2 reshape X of a / s1 and u = vec(P1^-1 X P2^-T) / s2 (the Kronecker
+    identity in row-major order, pinned against the dense form).  By default
+    the dense form is used when n <= 2048."""
+    a = np.asarray(a, dtype=np.float64)
+    B, n = a.shape
+    n1, n2 = p1_inv.shape[0], p2_inv.shape[0]
+    assert n1 * n2 == n
+    if dense is None:
+        dense = n <= 2048
+    if dense:
+        return a @ kron_inverse_dense(s1, p1_inv, p2_inv, s2_group, d).T
+    X = (a / np.asarray(s1, dtype=np.float64)[None, :]).reshape(B, n1, n2)
+    Y = np.asarray(p1_inv, dtype=np.float64)[None] @ X @ np.asarray(p2_inv, dtype=np.float64).T[None]
+    s2 = np.repeat(np.asarray(s2_group, dtype=np.float64), d)
+    return Y.reshape(B, n) / s2[None, :]
+
+
+def lift_kron(a, s1, p1_inv, p2_inv, s2_group, M, d: int, D: int, dtype: str) -> np.ndarray:
+    """a_hat = lift(T^-1 a) with the Kronecker T^-1, from the stored inputs
+    (a in `dtype`, the factors, scales and M float32) converted exactly."""
+    a64 = decode(a, dtype)
+    u = transform_kron(a64, decode(s1, "f32"), decode(p1_inv, "f32"), decode(p2_inv, "f32"),
+                       decode(s2_group, "f32"), d)
+    return lift(u, decode(M, "f32"), d, D)
+
+
+def forward_kron(packed: np.ndarray, K: int, M, s1, p1_inv, p2_inv, s2_group, s, a, d: int,
+                 D: int, dtype: str, rows: Optional[Sequence[int]] = None,
+                 chunk: int = 2048) -> np.ndarray:
+    """o by the reconstruct route with the Kronecker T^-1: unpack, W_hat = M y
+    per group, u = T^-1 a, o = s * (W_hat u)."""
+    M64, s64, a64 = decode(M, "f32"), decode(s, "f32"), decode(a, dtype)
+    u = transform_kron(a64, decode(s1, "f32"), decode(p1_inv, "f32"), decode(p2_inv, "f32"),
+                       decode(s2_group, "f32"), d)
+    idx = np.arange(packed.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = np.empty((a64.shape[0], idx.size), dtype=np.float64)
+    for c0 in range(0, idx.size, chunk):
+        sel = idx[c0:c0 + chunk]
+        w = reconstruct_weights(signs_from_packed(packed[sel], K), M64, d, D)
+        out[:, c0:c0 + sel.size] = (w @ u.T).T * s64[sel][None, :]
+    return out
 
 
 def _inputs64(M, t_inv, s, a, dtype):

@@ -286,3 +286,85 @@ def test_error_metric():
     ref = np.array([[1.0, -4.0, 2.0], [0.0, 0.0, 0.5]])
     got = ref + np.array([[0.0, 0.004, -0.002], [0.001, 0.0, 0.0]])
     assert O.rel_err_colmax(got, ref) == pytest.approx(max(0.004 / 4.0, 0.001 / 0.5))
+
+
+# ----------------------------------------------------------------- Kronecker whitening
+def _kron_lines():
+    for ln in _lines("kron_worked.txt"):
+        f = [np.array([float(x) for x in part.split()]) for part in ln.split(";")]
+        yield f
+
+
+def test_kron_worked_example():
+    """Hand-worked T^-1 a for 2 x 2 factors (tests/golden/kron_worked.txt), both routes."""
+    for a, s1, p1, p2, s2, want in _kron_lines():
+        for dense in (True, False):
+            u = O.transform_kron(a[None], s1, p1.reshape(2, 2), p2.reshape(2, 2), s2, 1, dense=dense)
+            np.testing.assert_allclose(u[0], want, rtol=0, atol=1e-14)
+
+
+def _orth(rng, n):
+    q, r = np.linalg.qr(rng.standard_normal((n, n)))
+    return q * np.sign(np.diag(r))[None, :]
+
+
+@pytest.mark.parametrize("n1,n2,d", [(3, 8, 4), (4, 16, 8), (8, 8, 2), (5, 12, 6)])
+def test_kron_round_trip_of_forward_T(n1, n2, d):
+    """transform_kron inverts the pages' forward T = diag(s1) (P1 (x) P2) diag(s2),
+    built densely from general (non-orthogonal) factors: T^-1 (T x) = x."""
+    rng = np.random.default_rng(n1 * 100 + n2 + d)
+    n = n1 * n2
+    P1 = rng.standard_normal((n1, n1)) + 3 * np.eye(n1)
+    P2 = rng.standard_normal((n2, n2)) + 3 * np.eye(n2)
+    s1 = rng.uniform(0.5, 2.0, n)
+    s2g = rng.uniform(0.5, 2.0, n // d)
+    T = np.diag(s1) @ np.kron(P1, P2) @ np.diag(np.repeat(s2g, d))
+    x = rng.standard_normal((3, n))
+    a = x @ T.T
+    for dense in (True, False):
+        u = O.transform_kron(a, s1, np.linalg.inv(P1), np.linalg.inv(P2), s2g, d, dense=dense)
+        np.testing.assert_allclose(u, x, rtol=1e-9, atol=1e-9)
+
+
+def test_kron_with_identity_first_factor_is_block_diagonal():
+    """P1 = I: P1^-1 (x) P2^-1 = blockdiag(P2^-1, ..., P2^-1), so with unit scales
+    the Kronecker transform equals the (separately pinned) block-diagonal one."""
+    rng = np.random.default_rng(7)
+    n1, n2 = 6, 16
+    p2 = rng.standard_normal((n2, n2))
+    a = rng.standard_normal((2, n1 * n2))
+    u = O.transform_kron(a, np.ones(n1 * n2), np.eye(n1), p2, np.ones(n1 * n2 // 4), 4, dense=False)
+    ref = O.transform(a, np.repeat(p2[None], n1, axis=0))
+    np.testing.assert_allclose(u, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_kron_hadamard_factors_preserve_norm():
+    """Normalised Sylvester-Hadamard factors (the pages' initialisation) are
+    orthogonal, so with unit scales T^-1 preserves the norm of every token."""
+    def had(k):
+        h = np.array([[1.0]])
+        while h.shape[0] < k:
+            h = np.block([[h, h], [h, -h]])
+        return h / np.sqrt(k)
+    rng = np.random.default_rng(8)
+    n1, n2 = 8, 32
+    H1, H2 = had(n1), had(n2)
+    a = rng.standard_normal((4, n1 * n2))
+    u = O.transform_kron(a, np.ones(n1 * n2), H1.T, H2.T, np.ones(n1 * n2 // 8), 8, dense=False)
+    np.testing.assert_allclose(np.linalg.norm(u, axis=1), np.linalg.norm(a, axis=1), rtol=1e-13)
+
+
+def test_kron_group_scale_folds_into_M():
+    """s2 constant over each d-group: lift(diag(1/s2) u) equals the lift with M
+    scaled per group by 1/s2 (the reason the pages can fold s2 into M)."""
+    rng = np.random.default_rng(9)
+    n1, n2, d, D = 4, 16, 8, 20
+    n = n1 * n2
+    a = rng.standard_normal((2, n))
+    p1, p2 = rng.standard_normal((n1, n1)), rng.standard_normal((n2, n2))
+    s1, s2g = rng.uniform(0.5, 2, n), rng.uniform(0.5, 2, n // d)
+    M = rng.standard_normal((d, D))
+    ah = O.lift(O.transform_kron(a, s1, p1, p2, s2g, d), M, d, D)
+    u1 = O.transform_kron(a, s1, p1, p2, np.ones(n // d), d)
+    folded = np.concatenate([(u1[:, g * d:(g + 1) * d] @ M) / s2g[g] for g in range(n // d)], axis=1)
+    np.testing.assert_allclose(ah, folded, rtol=1e-12, atol=1e-12)
