@@ -47,9 +47,10 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--gemm-dtype", default="f16", choices=["f16", "bf16"])
     p.add_argument("--no-cases", action="store_true", help="skip the per-workload sweep")
-    p.add_argument("--only", default="all", choices=["all", "layer", "gemm", "cases"],
+    p.add_argument("--only", default="all", choices=["all", "layer", "gemm", "cases", "kron"],
                    help="layer: only the timed 70B steps; gemm: only the batch-512 GEMM; "
-                        "cases: only the per-workload GEMV and lift sweep")
+                        "cases: only the per-workload GEMV and lift sweep; kron: only the "
+                        "Kronecker-whitened lift")
     return p.parse_args()
 
 
@@ -127,6 +128,8 @@ def run_gpu(args):
         return dict(gemm=run_gemm(args, torch, lq, synth, dev))
     if args.only == "cases":
         return dict(cases=run_cases(torch, lq, synth, dev))
+    if args.only == "kron":
+        return dict(kron=run_kron(torch, lq, synth, dev))
     cfg = synth.CONFIGS[3]                     # LQ-19/8 70B-class MLP
     layers = [synth.make_case(cfg, si, 1) for si in range(len(cfg.shapes))]
     rots = [Rotation(L, torch, lq, dev) for L in layers]
@@ -198,7 +201,8 @@ def run_gpu(args):
 
     gemm = None if args.only == "layer" else run_gemm(args, torch, lq, synth, dev)
     cases = None if (args.no_cases or args.only != "all") else run_cases(torch, lq, synth, dev)
-    return dict(value=value, ms_step=ms_step, roofline=roofline, gemm=gemm, cases=cases,
+    kron = None if args.only != "all" else run_kron(torch, lq, synth, dev)
+    return dict(value=value, ms_step=ms_step, roofline=roofline, gemm=gemm, cases=cases, kron=kron,
                 layers=layers, outs=outs_host, rot=rot_info, step_bytes=step_bytes)
 
 
@@ -271,6 +275,48 @@ def run_gemm(args, torch, lq, synth, dev):
                          "frac": round(tf / MFMA_PEAK_TFLOPS[args.gemm_dtype], 4),
                          "traffic": load_traffic("k_gemm.hip", "gemm_lq40_16_b512"),
                          "flops_per_launch": flops}}
+
+
+def kron_lift_bytes(n, n1, d, D, B, act_bytes=2, out_bytes=4):
+    """Algorithmic bytes of one Kronecker-whitened lift: a, s1, P1^-1, P2^-1,
+    s2, M and a_hat (the n1 x n2 intermediate's round trip excluded)."""
+    n2 = n // n1
+    return (B * n * act_bytes + 4 * n + 4 * n1 * n1 + 4 * n2 * n2 + 4 * (n // d) + 4 * d * D
+            + B * (n // d) * D * out_bytes)
+
+
+def run_kron(torch, lq, synth, dev):
+    """Lift with the Kronecker-factored whitening against the block-diagonal
+    lift on the same activations: the 70B-class shapes at batch 1 (float32
+    a_hat, as the GEMV takes) and LQ-40/16 at batch 512 (float16 a_hat)."""
+    res = []
+    st = torch.cuda.current_stream()
+    for cfg_i, si, B, odt in ((3, 0, 1, torch.float32), (3, 1, 1, torch.float32),
+                              (4, 0, 512, torch.float16)):
+        cfg = synth.CONFIGS[cfg_i]
+        L = synth.make_case(cfg, si, B, m=128)
+        f = synth.make_kron_factors(L.n, L.d, 1000 + si)
+        t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        s1, p1, p2, s2 = t(f.s1), t(f.p1_inv), t(f.p2_inv), t(f.s2)
+        M = t(L.M)
+        a = lq.to_torch_16(L.a, L.dtype).to(dev)
+        tinv = lq.to_torch_16(L.t_inv, L.dtype).to(dev)
+        out = torch.empty((B, L.K), dtype=odt, device=dev)
+        fn_k = lambda k: lq.lift_kron(a, s1, p1, p2, s2, M, L.d, L.D, out=out)
+        fn_b = lambda k: lq.lift(a, tinv, M, L.d, L.D, out=out)
+        fn_k(0)
+        fn_b(0)
+        torch.cuda.synchronize()
+        tk = graph_time(torch, fn_k, 20, 10, st)
+        tb = graph_time(torch, fn_b, 20, 10, st)
+        ob = 4 if odt == torch.float32 else 2
+        kb = kron_lift_bytes(L.n, f.n1, L.d, L.D, B, out_bytes=ob)
+        res.append({"case": f"{cfg.name} n={L.n} (n1 x n2 = {f.n1} x {f.n2}) B={B}",
+                    "kron_lift_us": round(tk * 1e3, 2), "kron_lift_GBs": round(kb / (tk * 1e-3) / 1e9, 1),
+                    "blockdiag_lift_us": round(tb * 1e3, 2),
+                    "whitening_bytes": {"kron": 4 * (L.n + f.n1 ** 2 + f.n2 ** 2 + L.n // L.d),
+                                        "blockdiag": 256 * L.n}})
+    return res
 
 
 def run_cases(torch, lq, synth, dev):
@@ -354,7 +400,7 @@ def main():
               f"(the path runs on one GPU; sharding over several is not built)", file=sys.stderr)
         sys.exit(2)
     r = run_gpu(args)
-    if args.only in ("gemm", "cases"):
+    if args.only in ("gemm", "cases", "kron"):
         print(json.dumps({args.only: r[args.only]}), flush=True)
         return
     cpu = None if args.no_cpu else cpu_baseline(r["layers"], r["outs"], args.cpu_seconds)
@@ -379,6 +425,7 @@ def main():
         "cpu_baseline": cpu,
         "gemm": r["gemm"],
         "cases": r["cases"],
+        "kron_lift": r["kron"],
     }
     print(json.dumps(line), flush=True)
 

@@ -114,6 +114,47 @@ lq_status lq_lift_activations(const void* a, lq_dtype a_dtype, int64_t B, int64_
                     "lq_lift_activations launch");
 }
 
+lq_status lq_lift_kron_workspace_size(int64_t B, int64_t n, size_t* bytes) {
+  if (!bytes) return fail(LQ_ERR_NULL, "bytes is null");
+  if (B < 1 || n < 1) return fail(LQ_ERR_SHAPE, "B=%lld n=%lld", (long long)B, (long long)n);
+  *bytes = lq::lift_kron_workspace_bytes(B, n);
+  return ok();
+}
+
+lq_status lq_lift_kron(const void* a, lq_dtype a_dtype, int64_t B, int64_t n, int32_t n1,
+                       const float* s1, const float* p1_inv, const float* p2_inv,
+                       const float* s2, const float* M, int32_t d, int32_t D, void* a_lift,
+                       lq_dtype lift_dtype, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  if (!a || !s1 || !p1_inv || !p2_inv || !s2 || !M || !a_lift || !workspace)
+    return fail(LQ_ERR_NULL, "null pointer");
+  if (!valid_dtype(a_dtype) || !valid_dtype(lift_dtype)) return fail(LQ_ERR_DTYPE, "unknown dtype");
+  if (B < 1 || n < 1) return fail(LQ_ERR_SHAPE, "B=%lld n=%lld", (long long)B, (long long)n);
+  if (d < 1 || d > 64 || D < 1 || D > 256 || d * D > 8192)
+    return fail(LQ_ERR_SHAPE, "d=%d D=%d out of range (1..64, 1..256, d*D <= 8192)", (int)d,
+                (int)D);
+  if (n > INT32_MAX || B > 65535 || (int64_t)n / d * D > INT32_MAX)
+    return fail(LQ_ERR_SHAPE, "B=%lld (<= 65535) or n exceed the launch limits", (long long)B);
+  if (n1 < 1 || n % n1 || n % d)
+    return fail(LQ_ERR_SHAPE, "n=%lld must be a multiple of n1=%d and d=%d", (long long)n, (int)n1,
+                (int)d);
+  if (!lq::lift_kron_shape_ok(n, n1, d, D))
+    return fail(LQ_ERR_UNSUPPORTED,
+                "n1=%d n2=%lld d=%d D=%d: needs n1 <= 256, n2 <= 128, n2 %% d == 0 and the "
+                "column tile in LDS", (int)n1, (long long)(n / n1), (int)d, (int)D);
+  if (workspace_bytes < lq::lift_kron_workspace_bytes(B, n))
+    return fail(LQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes,
+                lq::lift_kron_workspace_bytes(B, n));
+  if (!aligned(workspace, 256)) return fail(LQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (!aligned(a, dtype_size(a_dtype)) || !aligned(a_lift, dtype_size(lift_dtype)) ||
+      !aligned(s1, 4) || !aligned(p1_inv, 4) || !aligned(p2_inv, 4) || !aligned(s2, 4) ||
+      !aligned(M, 4))
+    return fail(LQ_ERR_ALIGN, "misaligned pointer");
+  return hip_status(lq::launch_lift_kron(a, a_dtype, B, n, n1, s1, p1_inv, p2_inv, s2, M, d, D,
+                                         a_lift, lift_dtype, workspace, as_stream(stream)),
+                    "lq_lift_kron launch");
+}
+
 lq_status lq_gemv_workspace_size(int64_t m, int64_t K, int64_t B, size_t* bytes) {
   if (!bytes) return fail(LQ_ERR_NULL, "bytes is null");
   if (m < 1 || K < 1 || B < 1 || B > 16)

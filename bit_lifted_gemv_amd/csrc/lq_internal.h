@@ -87,6 +87,14 @@ hipError_t launch_lift_mfma(const void* a, lq_dtype dt, int64_t B, int64_t n, co
                             const float* M, int d, int D, void* out, lq_dtype out_dt,
                             hipStream_t st);
 
+// Lift with the Kronecker-factored whitening (k_lift_kron.hip).
+bool lift_kron_shape_ok(int64_t n, int n1, int d, int D);
+size_t lift_kron_workspace_bytes(int64_t B, int64_t n);
+hipError_t launch_lift_kron(const void* a, lq_dtype a_dt, int64_t B, int64_t n, int n1,
+                            const float* s1, const float* p1_inv, const float* p2_inv,
+                            const float* s2, const float* M, int d, int D, void* out,
+                            lq_dtype out_dt, void* ws, hipStream_t st);
+
 // Compute units of the current device (cached per device).
 int num_cus();
 

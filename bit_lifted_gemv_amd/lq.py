@@ -24,8 +24,8 @@ STATUS = {0: "LQ_OK", 1: "LQ_ERR_NULL", 2: "LQ_ERR_SHAPE", 3: "LQ_ERR_DTYPE", 4:
           5: "LQ_ERR_UNSUPPORTED", 6: "LQ_ERR_HIP", 7: "LQ_ERR_WORKSPACE"}
 
 EXPORTS = ("lq_status_string", "lq_last_error", "lq_version", "lq_pack_signs", "lq_unpack_signs",
-           "lq_lift_activations", "lq_gemv_workspace_size", "lq_workspace_clear", "lq_gemv",
-           "lq_gemm")
+           "lq_lift_activations", "lq_lift_kron_workspace_size", "lq_lift_kron",
+           "lq_gemv_workspace_size", "lq_workspace_clear", "lq_gemv", "lq_gemm")
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -51,6 +51,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lq_unpack_signs": (_i32, [_vp, _i64, _i64, _i64, _vp, _i64, _vp]),
         "lq_lift_activations": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _i32, _vp, _i32, _i32,
                                        _vp, _i32, _vp]),
+        "lq_lift_kron_workspace_size": (_i32, [_i64, _i64, ctypes.POINTER(_sz)]),
+        "lq_lift_kron": (_i32, [_vp, _i32, _i64, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                _vp, _i32, _vp, _sz, _vp]),
         "lq_gemv_workspace_size": (_i32, [_i64, _i64, _i64, ctypes.POINTER(_sz)]),
         "lq_workspace_clear": (_i32, [_vp, _sz, _vp]),
         "lq_gemv": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
@@ -143,13 +146,35 @@ def lift(a: torch.Tensor, t_inv: torch.Tensor, M: torch.Tensor, d: int, D: int,
     return out
 
 
+def lift_kron(a: torch.Tensor, s1: torch.Tensor, p1_inv: torch.Tensor, p2_inv: torch.Tensor,
+              s2: torch.Tensor, M: torch.Tensor, d: int, D: int,
+              out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """a [B][n], Kronecker whitening factors (float32: s1 [n], P1^-1 [n1][n1],
+    P2^-1 [n2][n2], s2 [n/d]), M float [d][D] -> a_lift [B][n*D/d]."""
+    _dev(a, s1, p1_inv, p2_inv, s2, M)
+    B, n = a.shape
+    n1 = p1_inv.shape[0]
+    K = n // d * D
+    if out is None:
+        out = torch.empty((B, K), dtype=out_dtype, device=a.device)
+    nb = _sz(0)
+    check(lib().lq_lift_kron_workspace_size(B, n, ctypes.byref(nb)))
+    ws = workspace(nb.value, a.device, -1)
+    check(lib().lq_lift_kron(_ptr(a), _dt(a), B, n, n1, _ptr(s1), _ptr(p1_inv), _ptr(p2_inv),
+                             _ptr(s2), _ptr(M), d, D, _ptr(out), _dt(out), _ptr(ws), nb.value,
+                             _stream(stream)))
+    return out
+
+
 _WS = {}
 
 
-def workspace(nbytes: int, device: torch.device, m: int = 0) -> torch.Tensor:
-    """A GEMV workspace of at least nbytes, cached per (device, m) and grown
-    on demand (its contents need no initialisation)."""
-    key = (device.type, device.index, m)
+def workspace(nbytes: int, device: torch.device, tag: int = 0) -> torch.Tensor:
+    """A workspace of at least nbytes, cached per (device, tag) and grown on
+    demand (the library needs no initialisation of its contents).  The GEMV
+    uses its row count as tag, the Kronecker lift -1."""
+    key = (device.type, device.index, tag)
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)

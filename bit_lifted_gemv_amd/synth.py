@@ -194,6 +194,44 @@ def make_layer(m: int, n: int, d: int, D: int, B: int, seed: int, dtype: str = "
     return Layer(m, n, d, D, B, packed, M, t_inv, s, a, dtype, outliers.astype(np.int64))
 
 
+@dataclasses.dataclass
+class KronFactors:
+    """Kronecker-factored whitening of one layer, in the stored form the lift
+    takes: s1 [n], P1^-1 [n1][n1], P2^-1 [n2][n2], s2 [n/d], all float32."""
+    n1: int
+    n2: int
+    s1: np.ndarray
+    p1_inv: np.ndarray
+    p2_inv: np.ndarray
+    s2: np.ndarray
+
+
+def kron_split(n: int, d: int) -> Tuple[int, int]:
+    """n = n1 * n2 with n2 the largest divisor of n that is at most 128 and a
+    multiple of d (lift groups stay inside a row of the n1 x n2 reshape)."""
+    for n2 in range(min(128, n), 0, -1):
+        if n % n2 == 0 and n2 % d == 0:
+            return n // n2, n2
+    raise ValueError(f"no split of n={n} for d={d}")
+
+
+def make_kron_factors(n: int, d: int, seed: int, n1: Optional[int] = None) -> KronFactors:
+    """Seeded whitening factors: P1, P2 Haar orthogonal (so P^-1 = P^T),
+    s1 ~ U(0.5, 2) per channel, s2 ~ U(0.5, 2) per d-group.  Draw order:
+    P1, P2, s1, s2."""
+    if n1 is None:
+        n1, n2 = kron_split(n, d)
+    else:
+        n2 = n // n1
+    rng = np.random.default_rng(seed)
+    p1 = haar_orthogonal(rng, n1)
+    p2 = haar_orthogonal(rng, n2)
+    s1 = rng.uniform(0.5, 2.0, n).astype(np.float32)
+    s2 = rng.uniform(0.5, 2.0, n // d).astype(np.float32)
+    return KronFactors(n1, n2, s1, np.ascontiguousarray(p1.T).astype(np.float32),
+                       np.ascontiguousarray(p2.T).astype(np.float32), s2)
+
+
 def case_seed(cfg_index: int, shape_index: int) -> int:
     return 1000 * cfg_index + shape_index
 

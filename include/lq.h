@@ -103,6 +103,33 @@ lq_status lq_lift_activations(const void* a, lq_dtype a_dtype, int64_t B, int64_
                               void* a_lift, lq_dtype lift_dtype, void* stream);
 
 /*
+ * lq_lift_kron -- the lift with the Kronecker-factored whitening of
+ * 关键设计 3, T = diag(s1) (P1 (x) P2) diag(s2) with P1 n1 x n1, P2 n2 x n2,
+ * n = n1 n2 and s2 constant over each d-wide lift group (so that it folds
+ * into M):
+ *   u      = diag(1/s2) (P1^-1 (x) P2^-1) diag(1/s1) a
+ *   a_lift = (I (x) M^T) u,  a_lift[b][g*D + j] = sum_{r<d} M[r][j] u[b][g*d + r]
+ * Channel c = i*n2 + j of a token is entry (i, j) of its n1 x n2 reshape.
+ * a:        [B][n] of a_dtype (LQ_F16 | LQ_BF16 | LQ_F32).
+ * s1:       float [n];  s2: float [n/d] (one scale per group).
+ * p1_inv:   float [n1][n1] (P1^-1);  p2_inv: float [n2][n2] (P2^-1).
+ * M:        float [d][D].
+ * a_lift:   [B][K] of lift_dtype, K = n*D/d.
+ * workspace: device buffer of >= lq_lift_kron_workspace_size bytes (the
+ *           intermediate n1 x n2 products, float32), 256-byte aligned,
+ *           caller-owned, no initialisation needed.
+ * Requires 1 <= B <= 65535, n % n1 == 0, n2 = n/n1 <= 128, n1 <= 256,
+ * n2 % d == 0, 1 <= d <= 64, 1 <= D <= 256, d*D <= 8192 (else LQ_ERR_SHAPE or
+ * LQ_ERR_UNSUPPORTED, nothing launched).  float32 arithmetic throughout.
+ */
+lq_status lq_lift_kron_workspace_size(int64_t B, int64_t n, size_t* bytes);
+lq_status lq_lift_kron(const void* a, lq_dtype a_dtype, int64_t B, int64_t n, int32_t n1,
+                       const float* s1, const float* p1_inv, const float* p2_inv,
+                       const float* s2, const float* M, int32_t d, int32_t D, void* a_lift,
+                       lq_dtype lift_dtype, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
  * lq_gemv_workspace_size -- bytes of workspace lq_gemv needs for this shape
  * (0 when none).  Written to *bytes.
  */

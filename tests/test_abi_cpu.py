@@ -97,6 +97,33 @@ def test_lift_validation(L):
     assert ok  # the happy path needs a GPU and is covered by the GPU tests
 
 
+def test_lift_kron_validation(L):
+    F16 = lq.LQ_F16
+    nb = ctypes.c_size_t(0)
+    assert L.lq_lift_kron_workspace_size(4, 8192, ctypes.byref(nb)) == 0
+    assert nb.value >= 4 * 8192 * 4 and nb.value % 256 == 0
+    assert L.lq_lift_kron_workspace_size(0, 8192, ctypes.byref(nb)) == 2
+    WS = 1 << 20
+
+    def call(a=P, B=1, n=8192, n1=64, d=16, D=40, out=P, odt=0, ws=P, wsb=WS, s1=P):
+        return L.lq_lift_kron(a, F16, B, n, n1, s1, P, P, P, P, d, D, out, odt, ws, wsb, None)
+
+    assert call(a=None) == 1
+    assert call(ws=None) == 1
+    assert call(s1=None) == 1
+    assert call(odt=9) == 3
+    assert call(n1=60) == 2           # n not a multiple of n1
+    assert call(n1=32) == 5           # n2 = 256 > 128
+    assert call(n1=2048) == 5         # n1 > 256
+    assert call(n=8190, n1=63) == 2   # n not a multiple of d
+    assert call(n=8192, n1=128, d=48, D=48) == 2   # 8192 % 48 != 0
+    assert call(B=0) == 2
+    assert call(B=70000) == 2
+    assert call(wsb=16) == 7
+    assert call(ws=P + 16) == 4
+    assert call(s1=MIS) == 4
+
+
 def test_gemm_and_pack_validation(L):
     assert L.lq_gemm(P, 8, 64, 2, P, P, lq.LQ_F32, 512, P, None) == 3       # f32 activations
     assert L.lq_gemm(P, 8, 60, 2, P, P, lq.LQ_F16, 512, P, None) == 2       # K % 8

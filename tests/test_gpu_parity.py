@@ -107,6 +107,68 @@ def test_lift_16bit_outputs(dev, odt, n, d, D, B):
     assert (np.abs(got - ref) <= bound).all()
 
 
+# ----------------------------------------------------------------- lift, Kronecker whitening
+KRON_CASES = [  # (n, n1, d, D, B, act dtype): n2 = n / n1 <= 128, n2 % d == 0
+    (1280, 16, 10, 24, 1, "f16"), (512, 4, 8, 20, 3, "bf16"), (8192, 64, 16, 40, 1, "bf16"),
+    (8192, 64, 16, 40, 17, "f16"), (28672, 224, 8, 19, 1, "bf16"), (4096, 32, 8, 20, 5, "f32"),
+    (384, 3, 4, 9, 2, "bf16"), (960, 12, 8, 16, 7, "bf16"), (6, 2, 3, 5, 1, "f32"),
+    # large batches: several column blocks per wave, a ragged last column slab
+    (8192, 64, 16, 40, 512, "bf16"), (2048, 16, 8, 19, 300, "f16"),
+]
+
+
+def _kron_inputs(n, n1, d, D, B, dt, seed):
+    rng = np.random.default_rng(seed)
+    f = synth.make_kron_factors(n, d, seed, n1=n1)
+    M = (rng.standard_normal((d, D)) / np.sqrt(D)).astype(np.float32)
+    a = synth.to_storage(rng.standard_normal((B, n)).astype(np.float32), dt)
+    return f, M, a
+
+
+@pytest.mark.parametrize("n,n1,d,D,B,dt", KRON_CASES)
+def test_lift_kron_float32(dev, n, n1, d, D, B, dt):
+    _banner(f"lift_kron n={n} n1={n1} d={d} D={D} B={B} {dt}")
+    f, M, a = _kron_inputs(n, n1, d, D, B, dt, n + n1 + B)
+    ref = O.lift_kron(a, f.s1, f.p1_inv, f.p2_inv, f.s2, M, d, D, dt)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    got = lq.lift_kron(_up(a, dt, dev), t(f.s1), t(f.p1_inv), t(f.p2_inv), t(f.s2), t(M), d, D,
+                       out_dtype=torch.float32).cpu().numpy()
+    err = np.abs(got - ref).max(axis=1) / np.abs(ref).max(axis=1)
+    assert err.max() <= 1e-5, err
+
+
+@pytest.mark.parametrize("odt", [torch.float16, torch.bfloat16])
+def test_lift_kron_16bit_outputs(dev, odt):
+    n, n1, d, D, B = 8192, 64, 16, 40, 9
+    f, M, a = _kron_inputs(n, n1, d, D, B, "bf16", 77)
+    ref = O.lift_kron(a, f.s1, f.p1_inv, f.p2_inv, f.s2, M, d, D, "bf16")
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    got = lq.lift_kron(_up(a, "bf16", dev), t(f.s1), t(f.p1_inv), t(f.p2_inv), t(f.s2), t(M), d, D,
+                       out_dtype=odt).float().cpu().numpy()
+    u = 2.0 ** -11 if odt == torch.float16 else 2.0 ** -8
+    bound = u * np.abs(ref) + 1e-5 * np.abs(ref).max(axis=1, keepdims=True)
+    assert (np.abs(got - ref) <= bound).all()
+
+
+def test_layer_with_kron_whitening_70b_up(dev):
+    """The 70B-class up projection (28672 x 8192, LQ-19/8) with the Kronecker
+    whitening in place of the block-diagonal T^-1: lift_kron then the
+    one-token GEMV, against the oracle's reconstruct route on sampled rows."""
+    cfg = synth.CONFIGS[3]
+    L = synth.make_case(cfg, 0, 1)
+    f = synth.make_kron_factors(L.n, L.d, 123)
+    _banner(f"layer kron {L.m}x{L.n} n1={f.n1}")
+    dl = lq.DeviceLayer.from_synth(L, device=dev)
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+    al = lq.lift_kron(_up(L.a, L.dtype, dev), t(f.s1), t(f.p1_inv), t(f.p2_inv), t(f.s2), dl.M,
+                      L.d, L.D, out_dtype=torch.float32)
+    got = lq.gemv(dl.w, dl.s, al, L.K).cpu().numpy()
+    rows = _sample_rows(L.m, np.random.default_rng(5))
+    ref = O.forward_kron(L.packed, L.K, L.M, f.s1, f.p1_inv, f.p2_inv, f.s2, L.s, L.a, L.d, L.D,
+                         L.dtype, rows=rows)
+    assert O.rel_err_colmax(got[:, rows], ref) <= TOL_LUT16
+
+
 # ----------------------------------------------------------------- GEMV (lifted product)
 GEMV_CASES = [  # (m, K, B): ragged rows, slices and token groups
     (1, 4, 1), (63, 512, 1), (65, 516, 1), (200, 1544, 2), (129, 3072, 3), (300, 2048, 4),
