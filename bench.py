@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = {"f16": 2500.0, "bf16": 2500.0}   # dense
+PEAK_FP32_FLOPS = 157.3e12     # float32 matrix (and vector) peak, FLOP/s
 MALL_BYTES = 256 << 20
 METRIC = ("LQ GEMV achieved HBM GB/s (% of peak) at batch 1; "
           "MFMA TFLOP/s at batch 512")
@@ -285,6 +286,13 @@ def kron_lift_bytes(n, n1, d, D, B, act_bytes=2, out_bytes=4):
             + B * (n // d) * D * out_bytes)
 
 
+def kron_lift_flops(n, n1, D, B):
+    """Algorithmic flops of one Kronecker-whitened lift: per token the two
+    factor products, 2 n (n1 + n2), and the per-group M^T step, 2 n D."""
+    n2 = n // n1
+    return B * (2 * n * (n1 + n2) + 2 * n * D)
+
+
 def run_kron(torch, lq, synth, dev):
     """Lift with the Kronecker-factored whitening against the block-diagonal
     lift on the same activations: the 70B-class shapes at batch 1 (float32
@@ -311,8 +319,11 @@ def run_kron(torch, lq, synth, dev):
         tb = graph_time(torch, fn_b, 20, 10, st)
         ob = 4 if odt == torch.float32 else 2
         kb = kron_lift_bytes(L.n, f.n1, L.d, L.D, B, out_bytes=ob)
+        kf = kron_lift_flops(L.n, f.n1, L.D, B)
         res.append({"case": f"{cfg.name} n={L.n} (n1 x n2 = {f.n1} x {f.n2}) B={B}",
                     "kron_lift_us": round(tk * 1e3, 2), "kron_lift_GBs": round(kb / (tk * 1e-3) / 1e9, 1),
+                    "kron_lift_TFLOPs": round(kf / (tk * 1e-3) / 1e12, 2),
+                    "kron_lift_fp32_mfma_frac": round(kf / (tk * 1e-3) / PEAK_FP32_FLOPS, 4),
                     "blockdiag_lift_us": round(tb * 1e3, 2),
                     "whitening_bytes": {"kron": 4 * (L.n + f.n1 ** 2 + f.n2 ** 2 + L.n // L.d),
                                         "blockdiag": 256 * L.n}})
