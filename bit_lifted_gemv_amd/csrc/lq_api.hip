@@ -155,6 +155,40 @@ lq_status lq_lift_kron(const void* a, lq_dtype a_dtype, int64_t B, int64_t n, in
                     "lq_lift_kron launch");
 }
 
+lq_status lq_encode_workspace_size(int32_t d, int32_t D, size_t* bytes) {
+  if (!bytes) return fail(LQ_ERR_NULL, "bytes is null");
+  if (d < 1 || D < d || D > 32) return fail(LQ_ERR_SHAPE, "d=%d D=%d", (int)d, (int)D);
+  *bytes = lq::encode_workspace_bytes(D);
+  return ok();
+}
+
+lq_status lq_encode(const float* w, int64_t groups, const float* M, const float* A, int32_t d,
+                    int32_t D, int8_t* codes, float* err, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (groups < 0) return fail(LQ_ERR_SHAPE, "groups=%lld", (long long)groups);
+  if (d < 1 || D < d || D > 32)
+    return fail(LQ_ERR_SHAPE, "d=%d D=%d outside 1 <= d <= D <= 32", (int)d, (int)D);
+  if (A ? D - d > 24 : D > 24)
+    return fail(LQ_ERR_UNSUPPORTED, "%s over 2^%d candidates (at most 2^24)",
+                A ? "search" : "exhaustive search", A ? (int)(D - d) : (int)D);
+  if (groups > (int64_t)INT32_MAX * 4)
+    return fail(LQ_ERR_SHAPE, "groups=%lld exceeds the launch limits", (long long)groups);
+  if (groups == 0) return ok();
+  if (!w || !M || !codes) return fail(LQ_ERR_NULL, "null pointer");
+  if (A) {
+    if (!workspace) return fail(LQ_ERR_NULL, "workspace is null");
+    if (workspace_bytes < lq::encode_workspace_bytes(D))
+      return fail(LQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes,
+                  lq::encode_workspace_bytes(D));
+    if (!aligned(workspace, 256)) return fail(LQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+  }
+  if (!aligned(w, 4) || !aligned(M, 4) || (A && !aligned(A, 4)) || (err && !aligned(err, 4)))
+    return fail(LQ_ERR_ALIGN, "misaligned pointer");
+  return hip_status(lq::launch_encode(w, groups, M, A, d, D, codes, err, workspace,
+                                      as_stream(stream)),
+                    "lq_encode launch");
+}
+
 lq_status lq_gemv_workspace_size(int64_t m, int64_t K, int64_t B, size_t* bytes) {
   if (!bytes) return fail(LQ_ERR_NULL, "bytes is null");
   if (m < 1 || K < 1 || B < 1 || B > 16)

@@ -89,6 +89,10 @@ hipError_t launch_lift_mfma(const void* a, lq_dtype dt, int64_t B, int64_t n, co
 
 // Lift with the Kronecker-factored whitening (k_lift_kron.hip).
 bool lift_kron_shape_ok(int64_t n, int n1, int d, int D);
+size_t encode_workspace_bytes(int D);
+hipError_t launch_encode(const float* w, int64_t groups, const float* M, const float* A, int d,
+                         int D, int8_t* codes, float* err, void* ws, hipStream_t st);
+
 size_t lift_kron_workspace_bytes(int64_t B, int64_t n);
 hipError_t launch_lift_kron(const void* a, lq_dtype a_dt, int64_t B, int64_t n, int n1,
                             const float* s1, const float* p1_inv, const float* p2_inv,

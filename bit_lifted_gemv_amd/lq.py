@@ -25,7 +25,8 @@ STATUS = {0: "LQ_OK", 1: "LQ_ERR_NULL", 2: "LQ_ERR_SHAPE", 3: "LQ_ERR_DTYPE", 4:
 
 EXPORTS = ("lq_status_string", "lq_last_error", "lq_version", "lq_pack_signs", "lq_unpack_signs",
            "lq_lift_activations", "lq_lift_kron_workspace_size", "lq_lift_kron",
-           "lq_gemv_workspace_size", "lq_workspace_clear", "lq_gemv", "lq_gemm")
+           "lq_gemv_workspace_size", "lq_workspace_clear", "lq_gemv", "lq_gemm",
+           "lq_encode_workspace_size", "lq_encode")
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -58,6 +59,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lq_workspace_clear": (_i32, [_vp, _sz, _vp]),
         "lq_gemv": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
         "lq_gemm": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _i32, _i64, _vp, _vp]),
+        "lq_encode_workspace_size": (_i32, [_i32, _i32, ctypes.POINTER(_sz)]),
+        "lq_encode": (_i32, [_vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -167,13 +170,40 @@ def lift_kron(a: torch.Tensor, s1: torch.Tensor, p1_inv: torch.Tensor, p2_inv: t
     return out
 
 
+def encode(w: torch.Tensor, M: torch.Tensor, A: Optional[torch.Tensor] = None,
+           codes: Optional[torch.Tensor] = None, err: Optional[torch.Tensor] = None,
+           stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Lattice codes of float32 weight groups w [G][d] under M [d][D]:
+    exhaustive when A is None, else the auxiliary-vector search with the
+    completion A [D-d][D].  Returns (codes int8 [G][D], err float32 [G])."""
+    _dev(w, M)
+    G, d = w.shape
+    D = M.shape[1]
+    if codes is None:
+        codes = torch.empty((G, D), dtype=torch.int8, device=w.device)
+    if err is None:
+        err = torch.empty((G,), dtype=torch.float32, device=w.device)
+    ws, nbytes = None, 0
+    if A is not None:
+        _dev(A)
+        if A.numel() == 0:    # D == d: A has no rows; any non-null pointer selects the search
+            A = torch.zeros(1, dtype=torch.float32, device=w.device)
+        nb = _sz(0)
+        check(lib().lq_encode_workspace_size(d, D, ctypes.byref(nb)))
+        nbytes = nb.value
+        ws = workspace(nbytes, w.device, -2)
+    check(lib().lq_encode(_ptr(w), G, _ptr(M), _ptr(A), d, D, _ptr(codes), _ptr(err), _ptr(ws),
+                          nbytes, _stream(stream)))
+    return codes, err
+
+
 _WS = {}
 
 
 def workspace(nbytes: int, device: torch.device, tag: int = 0) -> torch.Tensor:
     """A workspace of at least nbytes, cached per (device, tag) and grown on
     demand (the library needs no initialisation of its contents).  The GEMV
-    uses its row count as tag, the Kronecker lift -1."""
+    uses its row count as tag, the Kronecker lift -1, the encoder -2."""
     key = (device.type, device.index, tag)
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:

@@ -130,6 +130,42 @@ lq_status lq_lift_kron(const void* a, lq_dtype a_dtype, int64_t B, int64_t n, in
                        void* stream);
 
 /*
+ * lq_encode -- quantise weight groups to lattice codes: for each d-wide group
+ * w, the code y in {+-1}^D whose projection M y is nearest to w (w ~ M y with
+ * M of shape d x D, 关键设计 1; the nearest-point search of 关键设计 2).
+ *   A == NULL: exhaustive, every y (2^D candidates; candidate t has y_j = +1
+ *              iff bit j of t is set).
+ *   A != NULL: the pseudo-inverse start plus auxiliary vector of 关键设计 2,
+ *              read as y(v) = sign([M; A]^-1 [w; v]) for every auxiliary sign
+ *              vector v in {+-1}^(D-d) (v_k = +1 iff bit k of t is set),
+ *              2^(D-d) candidates.  A ((D-d) x D) completes M to an
+ *              invertible matrix; with [M; A] orthogonal the candidate is
+ *              sign(M^+ w + A^T v).
+ * The candidate with the smallest ||w - M y||^2 is chosen, ties to the
+ * smallest t, sign(0) = +1.  Arithmetic is float32 (the inverse is formed in
+ * float64 and rounded), so groups whose best candidates are within float32
+ * rounding of each other may resolve to either.
+ * w:     float [groups][d] (group g is weights g*d .. g*d + d - 1; a weight
+ *        matrix [m][n] in row-major order is groups = m*n/d).
+ * M:     float [d][D];  A: float [D-d][D] or NULL (with D == d, A has no
+ *        rows: pass any non-null pointer to select the search).
+ * codes: int8 [groups][D], +1 / -1 (the lq_pack_signs input for a matrix of
+ *        m rows and K = n*D/d).
+ * err:   float [groups], the squared error of the chosen code, or NULL.
+ * workspace: with A, >= lq_encode_workspace_size bytes, 256-byte aligned,
+ *        caller-owned, no initialisation needed (it receives [M; A]^-1); may
+ *        be NULL without A.
+ * Requires 1 <= d <= D <= 32 and at most 2^24 candidates (D - d <= 24 with
+ * A, D <= 24 without); else LQ_ERR_SHAPE or LQ_ERR_UNSUPPORTED, nothing
+ * launched.  groups == 0 is a no-op.  A singular [M; A] gives unspecified
+ * codes.  Work grows as groups * 2^(D-d) (or 2^D) * d * D.
+ */
+lq_status lq_encode_workspace_size(int32_t d, int32_t D, size_t* bytes);
+lq_status lq_encode(const float* w, int64_t groups, const float* M, const float* A, int32_t d,
+                    int32_t D, int8_t* codes, float* err, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
  * lq_gemv_workspace_size -- bytes of workspace lq_gemv needs for this shape
  * (0 when none).  Written to *bytes.
  */

@@ -124,6 +124,31 @@ def test_lift_kron_validation(L):
     assert call(s1=MIS) == 4
 
 
+def test_encode_validation(L):
+    nb = ctypes.c_size_t(0)
+    assert L.lq_encode_workspace_size(8, 16, ctypes.byref(nb)) == 0
+    assert nb.value >= 16 * 16 * 4 and nb.value % 256 == 0
+    assert L.lq_encode_workspace_size(8, 33, ctypes.byref(nb)) == 2
+    WS = 1 << 12
+
+    def call(w=P, G=10, M=P, A=P, d=8, D=16, codes=P, err=P, ws=P, wsb=WS):
+        return L.lq_encode(w, G, M, A, d, D, codes, err, ws, wsb, None)
+
+    assert call(G=0, w=None, M=None, codes=None) == 0      # empty: no-op
+    assert call(w=None) == 1
+    assert call(codes=None) == 1
+    assert call(ws=None) == 1                              # the search needs the workspace
+    assert call(d=0) == 2
+    assert call(d=9, D=8) == 2                             # D < d
+    assert call(D=33) == 2
+    assert call(G=-1) == 2
+    assert call(d=4, D=30) == 5                            # 2^26 search candidates
+    assert call(A=None, d=8, D=25) == 5                    # 2^25 exhaustive candidates
+    assert call(wsb=16) == 7
+    assert call(ws=P + 16) == 4
+    assert call(err=MIS) == 4
+
+
 def test_gemm_and_pack_validation(L):
     assert L.lq_gemm(P, 8, 64, 2, P, P, lq.LQ_F32, 512, P, None) == 3       # f32 activations
     assert L.lq_gemm(P, 8, 60, 2, P, P, lq.LQ_F16, 512, P, None) == 2       # K % 8
