@@ -48,7 +48,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--gemm-dtype", default="f16", choices=["f16", "bf16"])
     p.add_argument("--no-cases", action="store_true", help="skip the per-workload sweep")
-    p.add_argument("--only", default="all", choices=["all", "layer", "gemm", "cases", "kron"],
+    p.add_argument("--only", default="all",
+                   choices=["all", "layer", "gemm", "cases", "kron", "encode"],
                    help="layer: only the timed 70B steps; gemm: only the batch-512 GEMM; "
                         "cases: only the per-workload GEMV and lift sweep; kron: only the "
                         "Kronecker-whitened lift")
@@ -131,6 +132,8 @@ def run_gpu(args):
         return dict(cases=run_cases(torch, lq, synth, dev))
     if args.only == "kron":
         return dict(kron=run_kron(torch, lq, synth, dev))
+    if args.only == "encode":
+        return dict(encode=run_encode(torch, lq, synth, dev))
     cfg = synth.CONFIGS[3]                     # LQ-19/8 70B-class MLP
     layers = [synth.make_case(cfg, si, 1) for si in range(len(cfg.shapes))]
     rots = [Rotation(L, torch, lq, dev) for L in layers]
@@ -203,7 +206,9 @@ def run_gpu(args):
     gemm = None if args.only == "layer" else run_gemm(args, torch, lq, synth, dev)
     cases = None if (args.no_cases or args.only != "all") else run_cases(torch, lq, synth, dev)
     kron = None if args.only != "all" else run_kron(torch, lq, synth, dev)
+    enc = None if args.only != "all" else run_encode(torch, lq, synth, dev)
     return dict(value=value, ms_step=ms_step, roofline=roofline, gemm=gemm, cases=cases, kron=kron,
+                encode=enc,
                 layers=layers, outs=outs_host, rot=rot_info, step_bytes=step_bytes)
 
 
@@ -284,6 +289,66 @@ def kron_lift_bytes(n, n1, d, D, B, act_bytes=2, out_bytes=4):
     n2 = n // n1
     return (B * n * act_bytes + 4 * n + 4 * n1 * n1 + 4 * n2 * n2 + 4 * (n // d) + 4 * d * D
             + B * (n // d) * D * out_bytes)
+
+
+# LiftQuant notes, table "Llama-2-7B Wikitext-2 PPL (标准 Gaussian 源)": code, D,
+# d, MSE (learned M) and search time per 1M parameters (s; "<<0.1" for
+# LQ-16/8), on the authors' hardware.
+ENCODE_TABLE = (("LQ-32/20", 32, 20, 0.146, 0.3), ("LQ-16/8", 16, 8, 0.089, "<<0.1"),
+                ("LQ-32/16", 32, 16, 0.082, 4.0), ("LQ-30/14", 30, 14, 0.070, 4.0),
+                ("LQ-24/10", 24, 10, 0.053, 1.0))
+# vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-operations per second
+# (one wave64 instruction every 4 cycles per SIMD; packed float32 is not used)
+ALU_PEAK_OPS = 256 * 4 * 16 * 2.4e9
+
+
+def run_encode(torch, lq, synth, dev):
+    """Lattice encoder over 1M unit-Gaussian weights per code of the table:
+    the auxiliary-vector search with M the first d rows of a Haar orthogonal
+    D x D matrix and A its other rows (the orthogonal initialisation; the
+    table's M is learned), plus the exhaustive search for LQ-16/8."""
+    res = []
+    n_params = 1_000_000
+    st = torch.cuda.current_stream()
+    runs = [(c, D, d, mse, ts, True) for c, D, d, mse, ts in ENCODE_TABLE]
+    runs.append(("LQ-16/8", 16, 8, 0.089, None, False))
+    for code, D, d, mse_tab, t_tab, search in runs:
+        G = -(-n_params // d)
+        Q = synth.haar_orthogonal(np.random.default_rng(1000 * D + d), D)   # same M per code
+        M = torch.from_numpy(Q[:d].astype(np.float32)).to(dev)
+        A = torch.from_numpy(Q[d:].astype(np.float32)).to(dev) if search else None
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(100 * D + d)
+        W = torch.randn((G, d), generator=gen, device=dev, dtype=torch.float32)
+        codes = torch.empty((G, D), dtype=torch.int8, device=dev)
+        err = torch.empty((G,), dtype=torch.float32, device=dev)
+        lq.encode(W, M, A, codes, err)
+        torch.cuda.synchronize()
+        reps = 3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            lq.encode(W, M, A, codes, err)
+        e1.record(st)
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / reps * 1e-3
+        kb = D - d if search else D
+        cands = G * (1 << kb)
+        ops = 2 * D + d * D + d if search else 2 * d      # per candidate, algorithmic
+        mse = float(err.double().sum().item()) / (G * d)
+        res.append({
+            "code": code, "mode": "search" if search else "exhaustive",
+            "candidates_per_group": 1 << kb, "groups": G,
+            "seconds_per_1M_weights": round(sec * n_params / (G * d), 5),
+            "candidates_per_s": float(f"{cands / sec:.4g}"),
+            "alu": {"bound": "alu", "achieved": float(f"{cands * ops / sec:.4g}"),
+                    "peak": ALU_PEAK_OPS, "unit": "lane-op/s",
+                    "frac": round(cands * ops / sec / ALU_PEAK_OPS, 4),
+                    "ops_per_candidate": ops},
+            "mse_per_weight": round(mse, 5), "info_bits": round(float(-0.5 * np.log2(mse)), 3),
+            "pages": {"mse_learned_M": mse_tab, "search_s_per_1M": t_tab,
+                      "note": "the authors' hardware and learned M: context, not a target"}})
+    return res
 
 
 def kron_lift_flops(n, n1, D, B):
@@ -411,7 +476,7 @@ def main():
               f"(the path runs on one GPU; sharding over several is not built)", file=sys.stderr)
         sys.exit(2)
     r = run_gpu(args)
-    if args.only in ("gemm", "cases", "kron"):
+    if args.only in ("gemm", "cases", "kron", "encode"):
         print(json.dumps({args.only: r[args.only]}), flush=True)
         return
     cpu = None if args.no_cpu else cpu_baseline(r["layers"], r["outs"], args.cpu_seconds)
@@ -437,6 +502,7 @@ def main():
         "gemm": r["gemm"],
         "cases": r["cases"],
         "kron_lift": r["kron"],
+        "encode": r["encode"],
     }
     print(json.dumps(line), flush=True)
 
