@@ -1,5 +1,5 @@
 """CPU oracle for the LiftQuant lattice encoder (nearest point of the projected
-1-bit lattice).
+1-bit lattice) and for learning the projection M.
 
 TEST INFRASTRUCTURE ONLY.  Imported by the tests and by the benchmark's
 CPU-baseline leg, never by the product path; it shares no code with the HIP
@@ -43,7 +43,8 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["sign_table", "encode_exhaustive", "encode_search", "search_matrix",
-           "group_errors", "info_bits", "codebook_mse"]
+           "group_errors", "info_bits", "codebook_mse", "softmin_objective", "adam_step",
+           "learn_m"]
 
 
 def sign_table(k: int) -> np.ndarray:
@@ -146,3 +147,86 @@ def codebook_mse(W: np.ndarray, M: np.ndarray, codes: np.ndarray) -> float:
     """Mean squared error per weight of the encoded groups (float64)."""
     W = np.asarray(W, dtype=np.float64)
     return float(group_errors(W, M, codes).sum() / W.size)
+
+
+# ----------------------------------------------------------- learning M
+# 关键设计 2: M* = argmin_M E_{w ~ N}[min_y ||w - M y||], M initialised
+# orthogonal, the inner argmin replaced by a soft-argmin at temperature 10 so
+# that the objective is differentiable and M is learned end to end.
+# Readings (also listed with the design notes):
+#   * the candidates are all 2^D codes (enumeration order as above);
+#   * soft-argmin: weights p_t = softmax_t(-T e_t) over the squared distances
+#     e_t = ||w - M y_t||^2 (T multiplies: T = 10 sharpens), and the soft code
+#     y_hat = sum_t p_t y_t replaces the argmin; the loss of a batch is the
+#     mean over its samples of ||w - M y_hat||^2;
+#   * the optimiser is Adam (the notes name none), textbook form below.
+
+
+def softmin_objective(W: np.ndarray, M: np.ndarray, T: float, chunk: int = 256):
+    """Soft-argmin objective of a batch W [N][d] and its gradient, float64.
+
+    Returns (loss, grad [d][D], y_hat [N][D]).  With r_n = w_n - M y_hat_n,
+    loss = mean_n ||r_n||^2.  Gradient, derived by the chain rule through
+    y_hat = P Y and P = softmax(-T E):
+      g_n  = -2 M^T r_n                      (d loss_n / d y_hat_n)
+      a_nt = g_n . y_t,  b_nt = p_nt (a_nt - g_n . y_hat_n)
+      dL/dM = (1/N) [ -2 sum_n r_n y_hat_n^T
+                      + 2T sum_t (sum_n b_nt w_n - beta_t C_t) y_t^T ],
+      C_t = M y_t, beta_t = sum_n b_nt."""
+    W = np.asarray(W, dtype=np.float64)
+    M = np.asarray(M, dtype=np.float64)
+    d, D = M.shape
+    N = W.shape[0]
+    Y = sign_table(D).astype(np.float64)               # [2^D][D]
+    C = Y @ M.T                                         # [2^D][d]
+    loss = 0.0
+    g_direct = np.zeros((d, D))
+    bw = np.zeros((1 << D, d))                          # sum_n b_nt w_n
+    beta = np.zeros(1 << D)
+    Yhat = np.zeros((N, D))
+    for s in range(0, N, chunk):
+        Wc = W[s:s + chunk]
+        E = ((Wc[:, None, :] - C[None, :, :]) ** 2).sum(axis=2)     # [n][2^D]
+        Z = -T * E
+        Z -= Z.max(axis=1, keepdims=True)
+        P = np.exp(Z)
+        P /= P.sum(axis=1, keepdims=True)
+        yh = P @ Y
+        R = Wc - yh @ M.T
+        loss += float((R * R).sum())
+        G = -2.0 * R @ M                                # [n][D]
+        A = G @ Y.T                                     # [n][2^D]
+        gy = (G * yh).sum(axis=1)
+        Bm = P * (A - gy[:, None])
+        g_direct += -2.0 * R.T @ yh
+        bw += Bm.T @ Wc
+        beta += Bm.sum(axis=0)
+        Yhat[s:s + chunk] = yh
+    dC = 2.0 * T * (bw - beta[:, None] * C)            # dL/dC_t, [2^D][d]
+    grad = (g_direct + dC.T @ Y) / N
+    return loss / N, grad, Yhat
+
+
+def adam_step(M, grad, m1, m2, step: int, lr: float, b1: float = 0.9, b2: float = 0.999,
+              eps: float = 1e-8):
+    """One Adam update (textbook, bias-corrected; step counts from 1).
+    Returns (M, m1, m2), all float64."""
+    m1 = b1 * np.asarray(m1, dtype=np.float64) + (1 - b1) * grad
+    m2 = b2 * np.asarray(m2, dtype=np.float64) + (1 - b2) * grad * grad
+    mh = m1 / (1 - b1 ** step)
+    vh = m2 / (1 - b2 ** step)
+    return np.asarray(M, dtype=np.float64) - lr * mh / (np.sqrt(vh) + eps), m1, m2
+
+
+def learn_m(batches, M0: np.ndarray, T: float, lr: float):
+    """Adam on the soft-argmin objective over the given sample batches (one
+    step per batch) from M0; returns (M, losses)."""
+    M = np.asarray(M0, dtype=np.float64).copy()
+    m1 = np.zeros_like(M)
+    m2 = np.zeros_like(M)
+    losses = []
+    for i, W in enumerate(batches, start=1):
+        loss, g, _ = softmin_objective(W, M, T)
+        M, m1, m2 = adam_step(M, g, m1, m2, i, lr)
+        losses.append(loss)
+    return M, losses

@@ -206,3 +206,110 @@ def test_codebook_mse_and_sign_table():
     W = np.array([[1.0, 2.0]])
     M = np.eye(2)
     assert C.codebook_mse(W, M, np.array([[1, 1]])) == pytest.approx(0.5)
+
+
+# ------------------------------------------------------------ learning M
+
+def test_softmin_gradient_matches_finite_differences():
+    """The derived gradient against central differences of the loss."""
+    rng = np.random.default_rng(20)
+    d, D, N, T = 2, 5, 9, 10.0
+    M = rng.standard_normal((d, D)) * 0.5
+    W = rng.standard_normal((N, d))
+    _, g, _ = C.softmin_objective(W, M, T)
+    h = 1e-6
+    fd = np.zeros_like(M)
+    for r in range(d):
+        for j in range(D):
+            Mp, Mm = M.copy(), M.copy()
+            Mp[r, j] += h
+            Mm[r, j] -= h
+            fd[r, j] = (C.softmin_objective(W, Mp, T)[0] - C.softmin_objective(W, Mm, T)[0]) / (2 * h)
+    np.testing.assert_allclose(g, fd, rtol=1e-6, atol=1e-8)
+
+
+def test_softmin_hard_limit_is_nearest_point_error():
+    """Large T: the soft code is the nearest code, so the loss is the mean
+    exhaustive nearest-point error."""
+    rng = np.random.default_rng(21)
+    d, D = 3, 7
+    M = _haar(rng, D)[:d]
+    W = rng.standard_normal((40, d))
+    loss, _, yh = C.softmin_objective(W, M, 1e6)
+    codes, err, _ = C.encode_exhaustive(W, M)
+    np.testing.assert_allclose(yh, codes, atol=1e-9)
+    assert abs(loss - err.mean()) < 1e-9
+
+
+def test_softmin_zero_temperature_is_uniform():
+    """T = 0: every code weighs 2^-D, the soft code is the mean of all sign
+    vectors (zero), the loss is mean ||w||^2 and the gradient vanishes."""
+    rng = np.random.default_rng(22)
+    M = rng.standard_normal((3, 6))
+    W = rng.standard_normal((11, 3))
+    loss, g, yh = C.softmin_objective(W, M, 0.0)
+    assert abs(loss - (W * W).sum(1).mean()) < 1e-12
+    np.testing.assert_allclose(yh, 0, atol=1e-15)
+    np.testing.assert_allclose(g, 0, atol=1e-12)
+
+
+def test_softmin_one_dimensional_closed_form():
+    """D = d = 1, M = [m]: y_hat = tanh(2 T m w), loss = mean (w - m y_hat)^2,
+    d loss / d m = mean 2 (w - m y_hat)(-y_hat - m (1 - y_hat^2) 2 T w)."""
+    rng = np.random.default_rng(23)
+    w = rng.standard_normal(50)
+    m, T = 0.8, 10.0
+    loss, g, yh = C.softmin_objective(w[:, None], np.array([[m]]), T)
+    th = np.tanh(2 * T * m * w)
+    np.testing.assert_allclose(yh[:, 0], th, rtol=1e-12, atol=1e-15)
+    assert abs(loss - np.mean((w - m * th) ** 2)) < 1e-12
+    dm = np.mean(2 * (w - m * th) * (-th - m * (1 - th ** 2) * 2 * T * w))
+    assert abs(g[0, 0] - dm) < 1e-10
+
+
+def test_softmin_column_sign_flip_and_permutation():
+    """The code set is closed under flipping a sign and permuting signs, so
+    flipping column j of M (or permuting columns) leaves the loss unchanged
+    and flips (permutes) the gradient the same way."""
+    rng = np.random.default_rng(24)
+    d, D = 3, 6
+    M = rng.standard_normal((d, D))
+    W = rng.standard_normal((20, d))
+    loss, g, _ = C.softmin_objective(W, M, 10.0)
+    Mf = M.copy()
+    Mf[:, 2] *= -1
+    lf, gf, _ = C.softmin_objective(W, Mf, 10.0)
+    assert abs(lf - loss) < 1e-12
+    gexp = g.copy()
+    gexp[:, 2] *= -1
+    np.testing.assert_allclose(gf, gexp, rtol=1e-10, atol=1e-12)
+    perm = rng.permutation(D)
+    lp, gp, _ = C.softmin_objective(W, M[:, perm], 10.0)
+    assert abs(lp - loss) < 1e-12
+    np.testing.assert_allclose(gp, g[:, perm], rtol=1e-10, atol=1e-12)
+
+
+def test_adam_first_step_is_signed_learning_rate():
+    """Step 1: bias correction makes m_hat = g and v_hat = g^2, so the update
+    is -lr g / (|g| + eps)."""
+    g = np.array([[0.5, -2.0], [1e-3, 0.0]])
+    M0 = np.zeros_like(g)
+    M1, m1, m2 = C.adam_step(M0, g, np.zeros_like(g), np.zeros_like(g), 1, lr=0.01)
+    np.testing.assert_allclose(M1, -0.01 * g / (np.abs(g) + 1e-8), rtol=1e-12)
+    np.testing.assert_allclose(m1, 0.1 * g)
+    np.testing.assert_allclose(m2, 0.001 * g * g)
+
+
+def test_learning_lowers_the_objective_and_the_codebook_error():
+    """From the orthogonal initialisation, Adam on the soft objective lowers
+    it and the hard nearest-point error of the learned M."""
+    rng = np.random.default_rng(25)
+    d, D = 4, 8
+    M0 = _haar(rng, D)[:d]
+    batches = [rng.standard_normal((256, d)) for _ in range(30)]
+    M, losses = C.learn_m(batches, M0, 10.0, 0.01)
+    assert np.mean(losses[-5:]) < losses[0]
+    Wt = np.random.default_rng(26).standard_normal((4000, d))
+    _, e0, _ = C.encode_exhaustive(Wt, M0)
+    _, e1, _ = C.encode_exhaustive(Wt, M)
+    assert e1.mean() < e0.mean()
