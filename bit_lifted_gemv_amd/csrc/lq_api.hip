@@ -155,6 +155,52 @@ lq_status lq_lift_kron(const void* a, lq_dtype a_dtype, int64_t B, int64_t n, in
                     "lq_lift_kron launch");
 }
 
+lq_status lq_softmin_workspace_size(int64_t N, int32_t d, int32_t D, size_t* bytes) {
+  if (!bytes) return fail(LQ_ERR_NULL, "bytes is null");
+  if (N < 1 || N > INT32_MAX || d < 1 || D < d || D > 24)
+    return fail(LQ_ERR_SHAPE, "N=%lld d=%d D=%d", (long long)N, (int)d, (int)D);
+  *bytes = lq::softmin_workspace_bytes(N, d, D);
+  return ok();
+}
+
+lq_status lq_softmin_grad(const float* w, int64_t N, const float* M, int32_t d, int32_t D,
+                          float T, float* loss, float* grad, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!w || !M || !loss || !grad || !workspace) return fail(LQ_ERR_NULL, "null pointer");
+  if (N < 1 || N > INT32_MAX) return fail(LQ_ERR_SHAPE, "N=%lld", (long long)N);
+  if (d < 1 || D < d || D > 32)
+    return fail(LQ_ERR_SHAPE, "d=%d D=%d outside 1 <= d <= D <= 32", (int)d, (int)D);
+  if (D > 24)
+    return fail(LQ_ERR_UNSUPPORTED, "D=%d: the soft-argmin runs over all 2^D codes (D <= 24)",
+                (int)D);
+  if (!(T >= 0.f) || !(T < 1e30f)) return fail(LQ_ERR_SHAPE, "T=%g must be finite and >= 0", T);
+  if (workspace_bytes < lq::softmin_workspace_bytes(N, d, D))
+    return fail(LQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes,
+                lq::softmin_workspace_bytes(N, d, D));
+  if (!aligned(workspace, 256)) return fail(LQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (!aligned(w, 4) || !aligned(M, 4) || !aligned(loss, 4) || !aligned(grad, 4))
+    return fail(LQ_ERR_ALIGN, "misaligned pointer");
+  return hip_status(lq::launch_softmin_grad(w, N, M, d, D, T, loss, grad, workspace,
+                                            as_stream(stream)),
+                    "lq_softmin_grad launch");
+}
+
+lq_status lq_adam_update(float* M, const float* grad, float* m1, float* m2, int64_t count,
+                         int32_t step, float lr, float beta1, float beta2, float eps,
+                         void* stream) {
+  if (count < 0) return fail(LQ_ERR_SHAPE, "count=%lld", (long long)count);
+  if (count == 0) return ok();
+  if (!M || !grad || !m1 || !m2) return fail(LQ_ERR_NULL, "null pointer");
+  if (step < 1 || !(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f) ||
+      !(eps >= 0.f))
+    return fail(LQ_ERR_SHAPE, "step=%d beta1=%g beta2=%g eps=%g", (int)step, beta1, beta2, eps);
+  if (!aligned(M, 4) || !aligned(grad, 4) || !aligned(m1, 4) || !aligned(m2, 4))
+    return fail(LQ_ERR_ALIGN, "misaligned pointer");
+  return hip_status(lq::launch_adam(M, grad, m1, m2, count, step, lr, beta1, beta2, eps,
+                                    as_stream(stream)),
+                    "lq_adam_update launch");
+}
+
 lq_status lq_encode_workspace_size(int32_t d, int32_t D, size_t* bytes) {
   if (!bytes) return fail(LQ_ERR_NULL, "bytes is null");
   if (d < 1 || D < d || D > 32) return fail(LQ_ERR_SHAPE, "d=%d D=%d", (int)d, (int)D);

@@ -89,6 +89,12 @@ hipError_t launch_lift_mfma(const void* a, lq_dtype dt, int64_t B, int64_t n, co
 
 // Lift with the Kronecker-factored whitening (k_lift_kron.hip).
 bool lift_kron_shape_ok(int64_t n, int n1, int d, int D);
+size_t softmin_workspace_bytes(int64_t N, int d, int D);
+hipError_t launch_softmin_grad(const float* W, int64_t N, const float* M, int d, int D, float T,
+                               float* loss, float* grad, void* ws, hipStream_t st);
+hipError_t launch_adam(float* M, const float* g, float* m1, float* m2, int64_t count, int step,
+                       float lr, float b1, float b2, float eps, hipStream_t st);
+
 size_t encode_workspace_bytes(int D);
 hipError_t launch_encode(const float* w, int64_t groups, const float* M, const float* A, int d,
                          int D, int8_t* codes, float* err, void* ws, hipStream_t st);

@@ -26,7 +26,8 @@ STATUS = {0: "LQ_OK", 1: "LQ_ERR_NULL", 2: "LQ_ERR_SHAPE", 3: "LQ_ERR_DTYPE", 4:
 EXPORTS = ("lq_status_string", "lq_last_error", "lq_version", "lq_pack_signs", "lq_unpack_signs",
            "lq_lift_activations", "lq_lift_kron_workspace_size", "lq_lift_kron",
            "lq_gemv_workspace_size", "lq_workspace_clear", "lq_gemv", "lq_gemm",
-           "lq_encode_workspace_size", "lq_encode")
+           "lq_encode_workspace_size", "lq_encode", "lq_softmin_workspace_size",
+           "lq_softmin_grad", "lq_adam_update")
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -61,6 +62,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lq_gemm": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _i32, _i64, _vp, _vp]),
         "lq_encode_workspace_size": (_i32, [_i32, _i32, ctypes.POINTER(_sz)]),
         "lq_encode": (_i32, [_vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+        "lq_softmin_workspace_size": (_i32, [_i64, _i32, _i32, ctypes.POINTER(_sz)]),
+        "lq_softmin_grad": (_i32, [_vp, _i64, _vp, _i32, _i32, ctypes.c_float, _vp, _vp, _vp,
+                                   _sz, _vp]),
+        "lq_adam_update": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, ctypes.c_float,
+                                  ctypes.c_float, ctypes.c_float, ctypes.c_float, _vp]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -197,13 +203,61 @@ def encode(w: torch.Tensor, M: torch.Tensor, A: Optional[torch.Tensor] = None,
     return codes, err
 
 
+def softmin_grad(w: torch.Tensor, M: torch.Tensor, T: float = 10.0,
+                 loss: Optional[torch.Tensor] = None, grad: Optional[torch.Tensor] = None,
+                 stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Soft-argmin objective of samples w [N][d] under M [d][D] and its
+    gradient: (loss float32 [1], grad float32 [d][D]), both on the device."""
+    _dev(w, M)
+    N, d = w.shape
+    D = M.shape[1]
+    if loss is None:
+        loss = torch.empty((1,), dtype=torch.float32, device=w.device)
+    if grad is None:
+        grad = torch.empty((d, D), dtype=torch.float32, device=w.device)
+    nb = _sz(0)
+    check(lib().lq_softmin_workspace_size(N, d, D, ctypes.byref(nb)))
+    ws = workspace(nb.value, w.device, -3)
+    check(lib().lq_softmin_grad(_ptr(w), N, _ptr(M), d, D, float(T), _ptr(loss), _ptr(grad),
+                                _ptr(ws), nb.value, _stream(stream)))
+    return loss, grad
+
+
+def adam_update(M: torch.Tensor, grad: torch.Tensor, m1: torch.Tensor, m2: torch.Tensor,
+                step: int, lr: float, beta1: float = 0.9, beta2: float = 0.999,
+                eps: float = 1e-8, stream=None) -> None:
+    """One Adam step on M in place (m1, m2: moment buffers, zero at step 1)."""
+    _dev(M, grad, m1, m2)
+    check(lib().lq_adam_update(_ptr(M), _ptr(grad), _ptr(m1), _ptr(m2), M.numel(), step,
+                               float(lr), float(beta1), float(beta2), float(eps),
+                               _stream(stream)))
+
+
+def learn_m(M0: torch.Tensor, batches, T: float = 10.0, lr: float = 0.01,
+            stream=None) -> Tuple[torch.Tensor, list]:
+    """Adam on the soft-argmin objective from M0, one step per batch of
+    samples (float32 [N][d] device tensors drawn by the caller).  Returns
+    (M, the per-step loss tensors)."""
+    M = M0.detach().clone().contiguous()
+    m1 = torch.zeros_like(M)
+    m2 = torch.zeros_like(M)
+    grad = torch.empty_like(M)
+    losses = []
+    for i, w in enumerate(batches, start=1):
+        loss, _ = softmin_grad(w, M, T, grad=grad, stream=stream)
+        adam_update(M, grad, m1, m2, i, lr, stream=stream)
+        losses.append(loss)
+    return M, losses
+
+
 _WS = {}
 
 
 def workspace(nbytes: int, device: torch.device, tag: int = 0) -> torch.Tensor:
     """A workspace of at least nbytes, cached per (device, tag) and grown on
     demand (the library needs no initialisation of its contents).  The GEMV
-    uses its row count as tag, the Kronecker lift -1, the encoder -2."""
+    uses its row count as tag, the Kronecker lift -1, the encoder -2, the
+    soft-argmin objective -3."""
     key = (device.type, device.index, tag)
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:

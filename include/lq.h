@@ -166,6 +166,40 @@ lq_status lq_encode(const float* w, int64_t groups, const float* M, const float*
                     size_t workspace_bytes, void* stream);
 
 /*
+ * lq_softmin_grad -- the objective that learns M (关键设计 2: M* minimises
+ * E_w[min_y ||w - M y||] over Gaussian w, M initialised orthogonal, the inner
+ * argmin replaced by a soft-argmin at temperature T, 10 in the notes) on one
+ * batch, and its gradient.  Over all 2^D codes y_t (y_tj = +1 iff bit j of t):
+ *   p_nt  = softmax_t(-T ||w_n - M y_t||^2),  y_hat_n = sum_t p_nt y_t,
+ *   *loss = (1/N) sum_n ||w_n - M y_hat_n||^2,   grad = d loss / d M.
+ * w:     float [N][d] samples (drawn by the caller).
+ * M:     float [d][D].
+ * loss:  device float (one value);  grad: float [d][D].
+ * workspace: >= lq_softmin_workspace_size bytes, 256-byte aligned,
+ *        caller-owned, no initialisation needed.
+ * Requires 1 <= N <= 2^31 - 1, 1 <= d <= D <= 24 (D <= 32 is a valid shape the
+ * build does not implement: LQ_ERR_UNSUPPORTED), T finite and >= 0.  float32
+ * arithmetic; the result does not depend on timing (fixed partition and
+ * summation order).  Work grows as N * 2^D * (d + D).
+ */
+lq_status lq_softmin_workspace_size(int64_t N, int32_t d, int32_t D, size_t* bytes);
+lq_status lq_softmin_grad(const float* w, int64_t N, const float* M, int32_t d, int32_t D,
+                          float T, float* loss, float* grad, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * lq_adam_update -- one Adam step on `count` floats in place (the optimiser
+ * that learns M; the notes name none, this is the textbook bias-corrected
+ * form): m1 = beta1 m1 + (1 - beta1) g, m2 = beta2 m2 + (1 - beta2) g^2,
+ * M -= lr (m1 / (1 - beta1^step)) / (sqrt(m2 / (1 - beta2^step)) + eps).
+ * m1, m2: caller-owned moment buffers, zero before step 1.  step >= 1,
+ * 0 <= beta1, beta2 < 1, eps >= 0; count == 0 is a no-op.
+ */
+lq_status lq_adam_update(float* M, const float* grad, float* m1, float* m2, int64_t count,
+                         int32_t step, float lr, float beta1, float beta2, float eps,
+                         void* stream);
+
+/*
  * lq_gemv_workspace_size -- bytes of workspace lq_gemv needs for this shape
  * (0 when none).  Written to *bytes.
  */

@@ -149,6 +149,36 @@ def test_encode_validation(L):
     assert call(err=MIS) == 4
 
 
+def test_softmin_and_adam_validation(L):
+    nb = ctypes.c_size_t(0)
+    assert L.lq_softmin_workspace_size(1000, 8, 16, ctypes.byref(nb)) == 0
+    assert nb.value > 0 and nb.value % 256 == 0
+    assert L.lq_softmin_workspace_size(0, 8, 16, ctypes.byref(nb)) == 2
+
+    def call(w=P, N=100, M=P, d=8, D=16, T=10.0, loss=P, grad=P, ws=P, wsb=1 << 30):
+        return L.lq_softmin_grad(w, N, M, d, D, T, loss, grad, ws, wsb, None)
+
+    assert call(w=None) == 1
+    assert call(ws=None) == 1
+    assert call(N=0) == 2
+    assert call(d=9, D=8) == 2
+    assert call(D=26) == 5                     # valid shape, not built (2^26 codes)
+    assert call(T=-1.0) == 2
+    assert call(T=float("nan")) == 2
+    assert call(wsb=16) == 7
+    assert call(ws=P + 4) == 4
+    assert call(grad=MIS) == 4
+
+    def adam(M=P, g=P, m1=P, m2=P, n=10, step=1, b1=0.9, b2=0.999):
+        return L.lq_adam_update(M, g, m1, m2, n, step, 0.01, b1, b2, 1e-8, None)
+
+    assert adam(n=0, M=None) == 0              # empty: no-op
+    assert adam(M=None) == 1
+    assert adam(step=0) == 2
+    assert adam(b1=1.0) == 2
+    assert adam(m2=MIS) == 4
+
+
 def test_gemm_and_pack_validation(L):
     assert L.lq_gemm(P, 8, 64, 2, P, P, lq.LQ_F32, 512, P, None) == 3       # f32 activations
     assert L.lq_gemm(P, 8, 60, 2, P, P, lq.LQ_F16, 512, P, None) == 2       # K % 8
