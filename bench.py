@@ -49,7 +49,7 @@ def parse():
     p.add_argument("--gemm-dtype", default="f16", choices=["f16", "bf16"])
     p.add_argument("--no-cases", action="store_true", help="skip the per-workload sweep")
     p.add_argument("--only", default="all",
-                   choices=["all", "layer", "gemm", "cases", "kron", "encode"],
+                   choices=["all", "layer", "gemm", "cases", "kron", "encode", "learn"],
                    help="layer: only the timed 70B steps; gemm: only the batch-512 GEMM; "
                         "cases: only the per-workload GEMV and lift sweep; kron: only the "
                         "Kronecker-whitened lift")
@@ -134,6 +134,8 @@ def run_gpu(args):
         return dict(kron=run_kron(torch, lq, synth, dev))
     if args.only == "encode":
         return dict(encode=run_encode(torch, lq, synth, dev))
+    if args.only == "learn":
+        return dict(learn=run_learn(torch, lq, synth, dev))
     cfg = synth.CONFIGS[3]                     # LQ-19/8 70B-class MLP
     layers = [synth.make_case(cfg, si, 1) for si in range(len(cfg.shapes))]
     rots = [Rotation(L, torch, lq, dev) for L in layers]
@@ -207,8 +209,9 @@ def run_gpu(args):
     cases = None if (args.no_cases or args.only != "all") else run_cases(torch, lq, synth, dev)
     kron = None if args.only != "all" else run_kron(torch, lq, synth, dev)
     enc = None if args.only != "all" else run_encode(torch, lq, synth, dev)
+    learn = None if args.only != "all" else run_learn(torch, lq, synth, dev)
     return dict(value=value, ms_step=ms_step, roofline=roofline, gemm=gemm, cases=cases, kron=kron,
-                encode=enc,
+                encode=enc, learn=learn,
                 layers=layers, outs=outs_host, rot=rot_info, step_bytes=step_bytes)
 
 
@@ -351,6 +354,54 @@ def run_encode(torch, lq, synth, dev):
     return res
 
 
+def run_learn(torch, lq, synth, dev):
+    """Learning M (soft-argmin objective at T = 10, Adam, lr 0.01) from the
+    orthogonal start on fresh unit-Gaussian batches: time per step, pair
+    throughput (samples x codes per second) and the hard nearest-point MSE
+    per weight of the start and the learned M (exhaustive encoder over 200k
+    fresh weights) beside the table's."""
+    res = []
+    st = torch.cuda.current_stream()
+    for code, d, D, N, steps, mse_tab in (("LQ-16/8", 8, 16, 4096, 400, 0.089),
+                                          ("LQ-20/8", 8, 20, 2048, 200, None)):
+        Q = synth.haar_orthogonal(np.random.default_rng(1000 * D + d), D)
+        M0 = torch.from_numpy(Q[:d].astype(np.float32)).to(dev)
+
+        def hard_mse(M, n=200_000):
+            g = torch.Generator(device=dev)
+            g.manual_seed(99)
+            W = torch.randn((n // d, d), generator=g, device=dev)
+            _, err = lq.encode(W, M)
+            return float(err.double().sum().item()) / n
+
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        batches = [torch.randn((N, d), generator=gen, device=dev) for _ in range(steps)]
+        M = M0.clone()
+        m1, m2, grad = torch.zeros_like(M), torch.zeros_like(M), torch.empty_like(M)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        last = None
+        for i, W in enumerate(batches, start=1):
+            last, _ = lq.softmin_grad(W, M, 10.0, grad=grad)
+            lq.adam_update(M, grad, m1, m2, i, 0.01)
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        pairs = N * (1 << D)
+        ops = pairs * (3 * d + D + 8 + 3 * d + D + 4)    # forward + backward, per pair
+        res.append({"code": code, "samples_per_step": N, "codes": 1 << D, "steps": steps,
+                    "ms_per_step": round(ms, 3),
+                    "pairs_per_s": float(f"{pairs / (ms * 1e-3):.4g}"),
+                    "alu_frac": round(ops / (ms * 1e-3) / ALU_PEAK_OPS, 4),
+                    "final_soft_loss": round(float(last.cpu()[0]), 5),
+                    "mse_orthogonal_start": round(hard_mse(M0), 5),
+                    "mse_learned": round(hard_mse(M), 5),
+                    "pages_mse_learned_M": mse_tab})
+    return res
+
+
 def kron_lift_flops(n, n1, D, B):
     """Algorithmic flops of one Kronecker-whitened lift: per token the two
     factor products, 2 n (n1 + n2), and the per-group M^T step, 2 n D."""
@@ -476,7 +527,7 @@ def main():
               f"(the path runs on one GPU; sharding over several is not built)", file=sys.stderr)
         sys.exit(2)
     r = run_gpu(args)
-    if args.only in ("gemm", "cases", "kron", "encode"):
+    if args.only in ("gemm", "cases", "kron", "encode", "learn"):
         print(json.dumps({args.only: r[args.only]}), flush=True)
         return
     cpu = None if args.no_cpu else cpu_baseline(r["layers"], r["outs"], args.cpu_seconds)
@@ -503,6 +554,7 @@ def main():
         "cases": r["cases"],
         "kron_lift": r["kron"],
         "encode": r["encode"],
+        "learn_m": r["learn"],
     }
     print(json.dumps(line), flush=True)
 
