@@ -155,6 +155,42 @@ lq_status lq_lift_kron(const void* a, lq_dtype a_dtype, int64_t B, int64_t n, in
                     "lq_lift_kron launch");
 }
 
+lq_status lq_gemm_decoded_workspace_size(int64_t m, int64_t n, size_t* bytes) {
+  if (!bytes) return fail(LQ_ERR_NULL, "bytes is null");
+  if (m < 1 || n < 1) return fail(LQ_ERR_SHAPE, "m=%lld n=%lld", (long long)m, (long long)n);
+  *bytes = lq::gemm_decoded_workspace_bytes(m, n);
+  return ok();
+}
+
+lq_status lq_gemm_decoded(const uint32_t* w_packed, int64_t m, int64_t n, int64_t ldw,
+                          const float* M, int32_t d, int32_t D, const float* s, const void* u,
+                          lq_dtype u_dtype, int64_t B, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (!w_packed || !M || !s || !u || !out || !workspace) return fail(LQ_ERR_NULL, "null pointer");
+  if (u_dtype != LQ_F16) return fail(LQ_ERR_DTYPE, "u must be LQ_F16");
+  if (m < 1 || n < 1 || B < 1 || m > INT32_MAX || n > INT32_MAX || B > INT32_MAX)
+    return fail(LQ_ERR_SHAPE, "m=%lld n=%lld B=%lld", (long long)m, (long long)n, (long long)B);
+  if (d < 1 || d > 64 || D < 1 || D > 256 || n % d)
+    return fail(LQ_ERR_SHAPE, "d=%d D=%d n=%lld (1 <= d <= 64, 1 <= D <= 256, n %% d == 0)",
+                (int)d, (int)D, (long long)n);
+  const int64_t K = n / d * D;
+  if (ldw < (K + 31) / 32) return fail(LQ_ERR_SHAPE, "ldw=%lld < ceil(K/32)", (long long)ldw);
+  if (!lq::gemm_decoded_shape_ok(d, D))
+    return fail(LQ_ERR_UNSUPPORTED, "d=%d D=%d: the decode tables exceed LDS", (int)d, (int)D);
+  if (workspace_bytes < lq::gemm_decoded_workspace_bytes(m, n))
+    return fail(LQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes,
+                lq::gemm_decoded_workspace_bytes(m, n));
+  if (!aligned(workspace, 256)) return fail(LQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+  if (!aligned(w_packed, 4) || !aligned(M, 4) || !aligned(s, 4) || !aligned(u, 2) ||
+      !aligned(out, 4))
+    return fail(LQ_ERR_ALIGN, "misaligned pointer");
+  const char* why = nullptr;
+  const hipError_t e = lq::launch_gemm_decoded(w_packed, m, n, ldw, M, d, D, s, u, B, out,
+                                               workspace, as_stream(stream), &why);
+  if (why) return fail(LQ_ERR_HIP, "lq_gemm_decoded: %s", why);
+  return hip_status(e, "lq_gemm_decoded launch");
+}
+
 lq_status lq_softmin_workspace_size(int64_t N, int32_t d, int32_t D, size_t* bytes) {
   if (!bytes) return fail(LQ_ERR_NULL, "bytes is null");
   if (N < 1 || N > INT32_MAX || d < 1 || D < d || D > 24)

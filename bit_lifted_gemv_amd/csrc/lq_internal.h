@@ -89,6 +89,14 @@ hipError_t launch_lift_mfma(const void* a, lq_dtype dt, int64_t B, int64_t n, co
 
 // Lift with the Kronecker-factored whitening (k_lift_kron.hip).
 bool lift_kron_shape_ok(int64_t n, int n1, int d, int D);
+bool gemm_decoded_shape_ok(int d, int D);
+int64_t gemm_decoded_chunk_rows(int64_t m, int64_t n);
+size_t gemm_decoded_workspace_bytes(int64_t m, int64_t n);
+hipError_t launch_gemm_decoded(const uint32_t* w, int64_t m, int64_t n, int64_t ldw,
+                               const float* M, int d, int D, const float* s, const void* u,
+                               int64_t B, float* out, void* ws, hipStream_t st,
+                               const char** why);
+
 size_t softmin_workspace_bytes(int64_t N, int d, int D);
 hipError_t launch_softmin_grad(const float* W, int64_t N, const float* M, int d, int D, float T,
                                float* loss, float* grad, void* ws, hipStream_t st);

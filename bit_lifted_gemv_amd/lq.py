@@ -27,7 +27,8 @@ EXPORTS = ("lq_status_string", "lq_last_error", "lq_version", "lq_pack_signs", "
            "lq_lift_activations", "lq_lift_kron_workspace_size", "lq_lift_kron",
            "lq_gemv_workspace_size", "lq_workspace_clear", "lq_gemv", "lq_gemm",
            "lq_encode_workspace_size", "lq_encode", "lq_softmin_workspace_size",
-           "lq_softmin_grad", "lq_adam_update")
+           "lq_softmin_grad", "lq_adam_update", "lq_gemm_decoded_workspace_size",
+           "lq_gemm_decoded")
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -63,6 +64,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lq_encode_workspace_size": (_i32, [_i32, _i32, ctypes.POINTER(_sz)]),
         "lq_encode": (_i32, [_vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
         "lq_softmin_workspace_size": (_i32, [_i64, _i32, _i32, ctypes.POINTER(_sz)]),
+        "lq_gemm_decoded_workspace_size": (_i32, [_i64, _i64, ctypes.POINTER(_sz)]),
+        "lq_gemm_decoded": (_i32, [_vp, _i64, _i64, _i64, _vp, _i32, _i32, _vp, _vp, _i32, _i64,
+                                   _vp, _vp, _sz, _vp]),
         "lq_softmin_grad": (_i32, [_vp, _i64, _vp, _i32, _i32, ctypes.c_float, _vp, _vp, _vp,
                                    _sz, _vp]),
         "lq_adam_update": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, ctypes.c_float,
@@ -203,6 +207,24 @@ def encode(w: torch.Tensor, M: torch.Tensor, A: Optional[torch.Tensor] = None,
     return codes, err
 
 
+def gemm_decoded(w_packed: torch.Tensor, s: torch.Tensor, M: torch.Tensor, d: int, D: int,
+                 u: torch.Tensor, out: Optional[torch.Tensor] = None,
+                 stream=None) -> torch.Tensor:
+    """out [B][m] = s * (W_hat @ u^T) with W_hat decoded from the signs and M
+    (float16 u [B][n], the whitened activations)."""
+    _dev(w_packed, s, M, u)
+    m, ldw = w_packed.shape
+    B, n = u.shape
+    if out is None:
+        out = torch.empty((B, m), dtype=torch.float32, device=u.device)
+    nb = _sz(0)
+    check(lib().lq_gemm_decoded_workspace_size(m, n, ctypes.byref(nb)))
+    ws = workspace(nb.value, u.device, -4)
+    check(lib().lq_gemm_decoded(_ptr(w_packed), m, n, ldw, _ptr(M), d, D, _ptr(s), _ptr(u),
+                                _dt(u), B, _ptr(out), _ptr(ws), nb.value, _stream(stream)))
+    return out
+
+
 def softmin_grad(w: torch.Tensor, M: torch.Tensor, T: float = 10.0,
                  loss: Optional[torch.Tensor] = None, grad: Optional[torch.Tensor] = None,
                  stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
@@ -257,7 +279,7 @@ def workspace(nbytes: int, device: torch.device, tag: int = 0) -> torch.Tensor:
     """A workspace of at least nbytes, cached per (device, tag) and grown on
     demand (the library needs no initialisation of its contents).  The GEMV
     uses its row count as tag, the Kronecker lift -1, the encoder -2, the
-    soft-argmin objective -3."""
+    soft-argmin objective -3, the decode-weights product -4."""
     key = (device.type, device.index, tag)
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
@@ -324,8 +346,14 @@ class DeviceLayer:
 
     def forward(self, a: torch.Tensor, gemm_dtype: torch.dtype = torch.float16,
                 path: str = "auto") -> torch.Tensor:
-        """o [B][m]: lift then the GEMV (B <= 16) or the GEMM (larger B)."""
+        """o [B][m]: lift then the GEMV (B <= 16) or the GEMM (larger B); with
+        path "decoded", u = T^-1 a (the lift with M = I_4) then the
+        decode-weights product."""
         B = a.shape[0]
+        if path == "decoded":
+            eye = torch.eye(4, dtype=torch.float32, device=a.device)
+            u = lift(a, self.t_inv, eye, 4, 4, out_dtype=torch.float16)
+            return gemm_decoded(self.w, self.s, self.M, self.d, self.D, u)
         use_gemm = path == "gemm" or (path == "auto" and B > 16)
         if use_gemm:
             al = lift(a, self.t_inv, self.M, self.d, self.D, out_dtype=gemm_dtype)

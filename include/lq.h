@@ -166,6 +166,37 @@ lq_status lq_encode(const float* w, int64_t groups, const float* M, const float*
                     size_t workspace_bytes, void* stream);
 
 /*
+ * lq_gemm_decoded -- the layer's product for large batches with the weights
+ * decoded instead of the activations lifted: W_hat[i][g*d + r] =
+ * sum_j M[r][j] sigma_{i, g*D + j} (w = M y, 关键设计 1), then
+ *   out[b][i] = s[i] * sum_{k<n} W_hat[i][k] * u[b][k],
+ * the same linear map as lq_gemm on the lifted activations (y . (M^T x) =
+ * (M y) . x), at 2 m n B + 2 m n D flops instead of 2 m K B (fewer once
+ * B > D d / (D - d)).
+ * w_packed: uint32 [m][ldw] (layout of lq_pack_signs), ldw >= ceil(K/32),
+ *           K = n*D/d.
+ * M:        float [d][D];  s: float [m].
+ * u:        float16 [B][n], the whitened activations T^-1 a (for example
+ *           lq_lift_activations with M = I_4, d = D = 4).
+ * out:      float [B][m].
+ * workspace: >= lq_gemm_decoded_workspace_size bytes (the decoded weights of
+ *           a chunk of rows, float16, s folded in), 256-byte aligned,
+ *           caller-owned, no initialisation needed.
+ * Arithmetic: decoded weights s[i] * W_hat rounded once to float16 (relative
+ * 2^-11), u in float16, products summed in float32 by a rocBLAS GEMM.
+ * Requires n % d == 0, 1 <= d <= 64, 1 <= D <= 256, m, n, B <= 2^31 - 1, the
+ * decode tables (ceil(D/8) x 256 x d floats, d rounded up to 4, 8, ..., 64)
+ * within 128 KB (else LQ_ERR_UNSUPPORTED); u must be LQ_F16 (else
+ * LQ_ERR_DTYPE).  A rocBLAS failure is reported as LQ_ERR_HIP.  The rocBLAS
+ * handle is created per device and host thread on first use.
+ */
+lq_status lq_gemm_decoded_workspace_size(int64_t m, int64_t n, size_t* bytes);
+lq_status lq_gemm_decoded(const uint32_t* w_packed, int64_t m, int64_t n, int64_t ldw,
+                          const float* M, int32_t d, int32_t D, const float* s, const void* u,
+                          lq_dtype u_dtype, int64_t B, float* out, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
  * lq_softmin_grad -- the objective that learns M (关键设计 2: M* minimises
  * E_w[min_y ||w - M y||] over Gaussian w, M initialised orthogonal, the inner
  * argmin replaced by a soft-argmin at temperature T, 10 in the notes) on one

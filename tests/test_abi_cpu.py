@@ -179,6 +179,28 @@ def test_softmin_and_adam_validation(L):
     assert adam(m2=MIS) == 4
 
 
+def test_gemm_decoded_validation(L):
+    nb = ctypes.c_size_t(0)
+    assert L.lq_gemm_decoded_workspace_size(8192, 8192, ctypes.byref(nb)) == 0
+    assert nb.value >= 2 * 8192 * 16 and nb.value % 256 == 0
+    F16, BF16 = lq.LQ_F16, lq.LQ_BF16
+
+    def call(w=P, m=64, n=512, ldw=40, M=P, d=16, D=40, s=P, u=P, udt=F16, B=8, out=P, ws=P,
+             wsb=1 << 30):
+        return L.lq_gemm_decoded(w, m, n, ldw, M, d, D, s, u, udt, B, out, ws, wsb, None)
+
+    assert call(w=None) == 1
+    assert call(ws=None) == 1
+    assert call(udt=BF16) == 3
+    assert call(n=500) == 2                  # n % d
+    assert call(ldw=39) == 2                 # K = 1280 needs 40 words
+    assert call(d=64, D=256, n=512, ldw=64) == 5   # tables beyond LDS
+    assert call(B=0) == 2
+    assert call(wsb=16) == 7
+    assert call(ws=P + 2) == 4
+    assert call(u=P + 1) == 4
+
+
 def test_gemm_and_pack_validation(L):
     assert L.lq_gemm(P, 8, 64, 2, P, P, lq.LQ_F32, 512, P, None) == 3       # f32 activations
     assert L.lq_gemm(P, 8, 60, 2, P, P, lq.LQ_F16, 512, P, None) == 2       # K % 8
