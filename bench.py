@@ -276,7 +276,9 @@ def run_gemm(args, torch, lq, synth, dev):
                          rot.R, n, st)
     flops = 2.0 * L.m * L.K * L.B
     tf = flops / (gemm_ms * 1e-3) / 1e12
+    decoded = run_decoded(torch, lq, L, rot, st, lift_ms + gemm_ms, n)
     return {"workload": f"LQ-40/16 {L.m}x{L.n} batch {L.B}, lifted K={L.K}",
+            "decoded": decoded,
             "operand_dtype": args.gemm_dtype, "gemm_us": round(gemm_ms * 1e3, 2),
             "lift_us": round(lift_ms * 1e3, 2), "tflops": round(tf, 1),
             "roofline": {"bound": "mfma", "achieved": round(tf, 1),
@@ -284,6 +286,43 @@ def run_gemm(args, torch, lq, synth, dev):
                          "frac": round(tf / MFMA_PEAK_TFLOPS[args.gemm_dtype], 4),
                          "traffic": load_traffic("k_gemm.hip", "gemm_lq40_16_b512"),
                          "flops_per_launch": flops}}
+
+
+def run_decoded(torch, lq, L, rot, st, lifted_ms, n_rep):
+    """The same batch on the decode-weights path: u = T^-1 a (lift with
+    M = I_4, float16), then decoded float16 weights s * (M y) contracted over
+    n (decode kernel + rocBLAS GEMM).  Own flop count: 2 m n B for the
+    product plus 2 m n D for the decoding.  Event timing of eager calls (the
+    call holds a library GEMM, kept out of graphs)."""
+    eye = torch.eye(4, dtype=torch.float32, device=rot.a.device)
+    u = torch.empty((L.B, L.n), dtype=torch.float16, device=rot.a.device)
+    out = torch.empty((L.B, L.m), dtype=torch.float32, device=rot.a.device)
+    for i in range(3):
+        lq.lift(rot.a, rot[i].t_inv, eye, 4, 4, out=u)
+        lq.gemm_decoded(rot[i].w, rot[i].s, rot[i].M, L.d, L.D, u, out=out)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for k in range(n_rep * rot.R):
+            fn(k % rot.R)
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (n_rep * rot.R)
+
+    lift_ms = timed(lambda k: lq.lift(rot.a, rot[k].t_inv, eye, 4, 4, out=u))
+    prod_ms = timed(lambda k: lq.gemm_decoded(rot[k].w, rot[k].s, rot[k].M, L.d, L.D, u,
+                                              out=out))
+    flops = 2.0 * L.m * L.n * L.B + 2.0 * L.m * L.n * L.D
+    tf = flops / (prod_ms * 1e-3) / 1e12
+    return {"lift_u_us": round(lift_ms * 1e3, 2), "decode_and_product_us": round(prod_ms * 1e3, 2),
+            "total_us": round((lift_ms + prod_ms) * 1e3, 2),
+            "lifted_path_total_us": round(lifted_ms * 1e3, 2),
+            "speedup_over_lifted": round(lifted_ms / (lift_ms + prod_ms), 3),
+            "flops_per_call": flops, "tflops": round(tf, 1),
+            "fp16_mfma_frac": round(tf / MFMA_PEAK_TFLOPS["f16"], 4),
+            "timing": "HIP events over eager calls on rotating copies"}
 
 
 def kron_lift_bytes(n, n1, d, D, B, act_bytes=2, out_bytes=4):

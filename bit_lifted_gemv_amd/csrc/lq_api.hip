@@ -176,7 +176,7 @@ lq_status lq_gemm_decoded(const uint32_t* w_packed, int64_t m, int64_t n, int64_
   const int64_t K = n / d * D;
   if (ldw < (K + 31) / 32) return fail(LQ_ERR_SHAPE, "ldw=%lld < ceil(K/32)", (long long)ldw);
   if (!lq::gemm_decoded_shape_ok(d, D))
-    return fail(LQ_ERR_UNSUPPORTED, "d=%d D=%d: the decode tables exceed LDS", (int)d, (int)D);
+    return fail(LQ_ERR_UNSUPPORTED, "d=%d D=%d beyond the decode tiles", (int)d, (int)D);
   if (workspace_bytes < lq::gemm_decoded_workspace_bytes(m, n))
     return fail(LQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes,
                 lq::gemm_decoded_workspace_bytes(m, n));

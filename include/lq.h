@@ -182,12 +182,12 @@ lq_status lq_encode(const float* w, int64_t groups, const float* M, const float*
  * workspace: >= lq_gemm_decoded_workspace_size bytes (the decoded weights of
  *           a chunk of rows, float16, s folded in), 256-byte aligned,
  *           caller-owned, no initialisation needed.
- * Arithmetic: decoded weights s[i] * W_hat rounded once to float16 (relative
- * 2^-11), u in float16, products summed in float32 by a rocBLAS GEMM.
- * Requires n % d == 0, 1 <= d <= 64, 1 <= D <= 256, m, n, B <= 2^31 - 1, the
- * decode tables (ceil(D/8) x 256 x d floats, d rounded up to 4, 8, ..., 64)
- * within 128 KB (else LQ_ERR_UNSUPPORTED); u must be LQ_F16 (else
- * LQ_ERR_DTYPE).  A rocBLAS failure is reported as LQ_ERR_HIP.  The rocBLAS
+ * Arithmetic: the weights are decoded on the matrix cores from M rounded to
+ * float16 (exact +-1 signs, float32 sums), scaled by s[i] and rounded to
+ * float16 (relative 2^-11 each); u in float16; the product sums in float32
+ * (rocBLAS GEMM).
+ * Requires n % d == 0, 1 <= d <= 64, 1 <= D <= 256, m, n, B <= 2^31 - 1; u
+ * must be LQ_F16 (else LQ_ERR_DTYPE).  A rocBLAS failure is reported as LQ_ERR_HIP.  The rocBLAS
  * handle is created per device and host thread on first use.
  */
 lq_status lq_gemm_decoded_workspace_size(int64_t m, int64_t n, size_t* bytes);

@@ -194,7 +194,7 @@ def test_gemm_decoded_validation(L):
     assert call(udt=BF16) == 3
     assert call(n=500) == 2                  # n % d
     assert call(ldw=39) == 2                 # K = 1280 needs 40 words
-    assert call(d=64, D=256, n=512, ldw=64) == 5   # tables beyond LDS
+    assert call(d=65, n=520, ldw=64) == 2    # d > 64
     assert call(B=0) == 2
     assert call(wsb=16) == 7
     assert call(ws=P + 2) == 4

@@ -36,6 +36,7 @@ CASES = [  # (m, n, d, D, B, dtype): LQ-40/16, LQ-19/8 (groups straddle words),
     (256, 512, 16, 40, 130, "bf16"), (200, 1024, 8, 19, 40, "bf16"),
     (130, 1280, 10, 24, 17, "f16"), (64, 384, 3, 7, 33, "bf16"), (48, 512, 8, 8, 20, "f16"),
     (33, 256, 16, 33, 5, "bf16"), (17, 256, 8, 16, 1, "bf16"), (300, 2048, 8, 16, 64, "bf16"),
+    (40, 640, 32, 70, 9, "bf16"), (24, 384, 48, 129, 3, "bf16"),
 ]
 
 
