@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--gemm-dtype", default="f16", choices=["f16", "bf16"])
     p.add_argument("--no-cases", action="store_true", help="skip the per-workload sweep")
+    p.add_argument("--layer-path", default="split", choices=["fused", "split"],
+                   help="one-token step: the lift inside the GEMV (lq_layer_b1) or the lift "
+                        "and the GEMV as two calls")
     p.add_argument("--only", default="all",
                    choices=["all", "layer", "gemm", "cases", "kron", "encode", "learn"],
                    help="layer: only the timed 70B steps; gemm: only the batch-512 GEMM; "
@@ -144,66 +147,91 @@ def run_gpu(args):
     al = [torch.empty((1, L.K), dtype=torch.float32, device=dev) for L in layers]
     outs = [torch.empty((1, L.m), dtype=torch.float32, device=dev) for L in layers]
 
-    def step(i):
+    def step_fused(i):
+        for j, (rot, L) in enumerate(zip(rots, layers)):
+            c = rot[i]
+            lq.layer_b1(rot.a, c.t_inv, c.M, L.d, L.D, c.w, c.s, out=outs[j])
+
+    def step_split(i):
         for j, (rot, L) in enumerate(zip(rots, layers)):
             c = rot[i]
             lq.lift(rot.a, c.t_inv, c.M, L.d, L.D, out=al[j])
             lq.gemv(c.w, c.s, al[j], L.K, out=outs[j])
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # One HIP graph per weight copy, each one whole step, so that the timed
-    # loop measures the GPU, not the host's launch rate.  Every graph's replay
-    # is checked bit for bit against the eager step on the same copy.
     R = rots[0].R
-    graphs = capture_graphs(torch, [lambda k=k: step(k) for k in range(R)])
-    for k in range(R):
-        step(k)
+
+    def time_step(step, steps):
+        """Warm up, capture one HIP graph per weight copy (each one whole
+        step, so that the timed loop measures the GPU, not the host's launch
+        rate), check every replay bit for bit against the eager step on the
+        same copy, then time `steps` replays between synchronisations."""
+        for i in range(args.warmup):
+            step(i)
         torch.cuda.synchronize()
-        want = [o.clone() for o in outs]
-        for o in outs:
-            o.fill_(float("nan"))
-        graphs[k].replay()
+        graphs = capture_graphs(torch, [lambda k=k: step(k) for k in range(R)])
+        for k in range(R):
+            step(k)
+            torch.cuda.synchronize()
+            want = [o.clone() for o in outs]
+            for o in outs:
+                o.fill_(float("nan"))
+            graphs[k].replay()
+            torch.cuda.synchronize()
+            for o, w in zip(outs, want):
+                if not torch.equal(o, w):
+                    raise RuntimeError(f"graph replay {k} differs from the eager step")
         torch.cuda.synchronize()
-        for o, w in zip(outs, want):
-            if not torch.equal(o, w):
-                raise RuntimeError(f"graph replay {k} differs from the eager step")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        graphs[(args.warmup + i) % R].replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
+        t0 = time.perf_counter()
+        for i in range(steps):
+            graphs[(args.warmup + i) % R].replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        return (t1 - t0) * 1e3 / steps
+
+    fused = args.layer_path == "fused"
+    ms_step = time_step(step_fused if fused else step_split, args.steps)
+    ms_other = time_step(step_split if fused else step_fused, max(3, min(args.steps, 20)))
     step_bytes = sum(layer_bytes(L.m, L.n, L.d, L.D, 1) for L in layers)
     value = step_bytes / (ms_step * 1e-3) / 1e9
 
-    # dominant kernel: the one-token GEMV call; per-call duration from HIP
-    # events around replays of a graph of back-to-back calls over the copies
+    # dominant kernel: the one-token layer call (fused: lq_layer_b1, its
+    # stream kernel with the lift in the table prologue plus the slice
+    # reduction; split: the lq_gemv call); per-call duration from HIP events
+    # around replays of a graph of back-to-back calls over the copies
     per = {}
     for j, (rot, L) in enumerate(zip(rots, layers)):
-        g = capture_graphs(torch, [lambda: [lq.gemv(rot[k].w, rot[k].s, al[j], L.K, out=outs[j])
-                                            for k in range(R)]])[0]
+        if fused:
+            calls = lambda: [lq.layer_b1(rot.a, rot[k].t_inv, rot[k].M, L.d, L.D, rot[k].w,
+                                         rot[k].s, out=outs[j]) for k in range(R)]
+        else:
+            calls = lambda: [lq.gemv(rot[k].w, rot[k].s, al[j], L.K, out=outs[j])
+                             for k in range(R)]
+        g = capture_graphs(torch, [calls])[0]
         n_rep = max(3, min(args.steps, 20))
         per[j] = time_launches(torch, lambda i: g.replay(), n_rep, st) / R
-    g_bytes = [gemv_bytes(L.m, L.K, 1) for L in layers]
+    g_bytes = [layer_bytes(L.m, L.n, L.d, L.D, 1) if fused else gemv_bytes(L.m, L.K, 1)
+               for L in layers]
     gemv_ms = sum(per.values()) / len(per)
     gemv_bytes_avg = sum(g_bytes) / len(g_bytes)
     achieved = gemv_bytes_avg / (gemv_ms * 1e-3) / 1e9
-    traffic = load_traffic("k_gemv1.hip", "gemv_lq19_8_70b_b1")
+    traffic = load_traffic("k_gemv1.hip", "layer_b1_lq19_8_70b" if fused else
+                           "gemv_lq19_8_70b_b1")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "lq_gemv B=1 (gemv1_kernel + gemv1_reduce_kernel)",
+                "kernel": ("lq_layer_b1 (gemv1_kernel with the lift in its table prologue + "
+                           "gemv1_reduce_kernel)" if fused else
+                           "lq_gemv B=1 (gemv1_kernel + gemv1_reduce_kernel)"),
                 "bytes_per_launch": int(gemv_bytes_avg),
                 "avg_launch_us": round(gemv_ms * 1e3, 3),
                 "per_shape_us": {f"{L.m}x{L.n}": round(per[j] * 1e3, 3)
                                  for j, L in enumerate(layers)}}
-    step(0)
+    (step_fused if fused else step_split)(0)
     torch.cuda.synchronize()
     outs_host = [o.cpu().numpy().copy() for o in outs]
     rot_info = {"copies": rots[0].R, "bytes_per_copy": int(layers[0].packed.nbytes),
-                "timing": "HIP graph per step, replayed; checked bit for bit against eager"}
+                "timing": "HIP graph per step, replayed; checked bit for bit against eager",
+                "path": args.layer_path,
+                "other_path_ms_per_step": round(ms_other, 5)}
 
     gemm = None if args.only == "layer" else run_gemm(args, torch, lq, synth, dev)
     cases = None if (args.no_cases or args.only != "all") else run_cases(torch, lq, synth, dev)

@@ -155,6 +155,52 @@ __device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
   return u;
 }
 
+// Inputs of the lift when it runs in the kernel's table prologue (the fused
+// one-token layer): a [n] and the block-diagonal T^-1 [n/128][128][128] of
+// one element type, M [d][D].
+struct LiftIn {
+  const void* a;
+  const void* t;
+  const float* M;
+  int d;
+  int D;
+};
+
+// 16 consecutive elements at index i (a multiple of 8), raw: two 16-byte
+// vectors for 16-bit types (r[0..1]), four for float32 (r[0..3]).
+template <int DT>
+__device__ __forceinline__ void load16raw(const void* base, int64_t i, uint4 (&r)[4]) {
+  if constexpr (DT == LQ_F32) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const float*>(base) + i);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r[k] = p[k];
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + i);
+    r[0] = p[0];
+    r[1] = p[1];
+  }
+}
+
+// Element k (< 16) of a raw run.
+template <int DT>
+__device__ __forceinline__ float raw_elem(const uint4 (&r)[4], int k) {
+  if constexpr (DT == LQ_F32) {
+    const uint4 q = r[k >> 2];
+    const uint32_t wv = (k & 3) == 0 ? q.x : (k & 3) == 1 ? q.y : (k & 3) == 2 ? q.z : q.w;
+    return __uint_as_float(wv);
+  } else {
+    const uint4 q = r[k >> 3];
+    const int h = (k & 7) >> 1;
+    const uint32_t wv = h == 0 ? q.x : h == 1 ? q.y : h == 2 ? q.z : q.w;
+    if constexpr (DT == LQ_BF16)
+      return __uint_as_float((k & 1) ? (wv & 0xFFFF0000u) : (wv << 16));
+    else
+      return f16_bits_to_float(static_cast<uint16_t>((k & 1) ? (wv >> 16) : (wv & 0xFFFFu)));
+  }
+}
+
+constexpr int kMaxLiftCh = kSliceBits + 2 * 64;   // channels behind one slice (D >= d, d <= 64)
+
 // Float16 table of one slice, built by the WAVES waves.  Flipping every bit
 // of a weight byte flips every sign, so E[255 - v] = -E[v]: wave w computes
 // the entries of v in [VB w, VB w + VB), VB = 128 / WAVES (low bits of v in
@@ -197,12 +243,20 @@ __device__ __forceinline__ void build_table16(uint16_t* __restrict__ tab, const 
   }
 }
 
-template <bool SPLIT>
+// LDT < 0: the lifted activations a_hat come from memory.  LDT = the element
+// type of a and T^-1: the table prologue computes the slice's a_hat itself
+// (the fused layer): u = T^-1 a for the slice's channels, 8 lanes per
+// channel with 16 of the 128 terms each (added across the 8 lanes), then
+// a_hat[g D + j] = sum_r M[r][j] u[g d + r], one position per thread.
+template <bool SPLIT, int LDT>
 __global__ void __launch_bounds__(kThreads, 1) gemv1_kernel(
     const uint32_t* __restrict__ w, int64_t m, int64_t K, int64_t ldw,
     const float* __restrict__ s, const float* __restrict__ ah, float* __restrict__ out,
-    float* __restrict__ partials, Sched1 sc, uint32_t w_bytes, uint32_t a_bytes) {
+    float* __restrict__ partials, Sched1 sc, uint32_t w_bytes, uint32_t a_bytes, LiftIn li) {
   __shared__ __attribute__((aligned(16))) uint16_t tabs[2 * kTableHalves];   // 128 KB
+  constexpr bool kFused = LDT >= 0;
+  __shared__ __attribute__((aligned(16))) float ul[kFused ? kMaxLiftCh : 1];   // u of the slice
+  __shared__ __attribute__((aligned(16))) float xs[kFused ? 2 * kSliceBits : 1];  // a_hat
   static_assert(kWaves >= 8 && (kWaves & (kWaves - 1)) == 0 && kWaves <= 32, "8..32 waves");
   constexpr int D = kDepth;
   const int tid = threadIdx.x;
@@ -309,22 +363,101 @@ __global__ void __launch_bounds__(kThreads, 1) gemv1_kernel(
   // once would stall on the full memory queue).
   uint4 wb[D][2];
   float scale_up[2];
+  // Fused layer: a_hat of slice sl into xs[t * 1024 ..] (zero past K).  The
+  // T^-1 rows and activations of up to 3 passes of 128 channels are loaded
+  // before any is used; `first` issues the workgroup's first two granules
+  // of weights after the first loads, so they stream during the lift.
+  auto lift_slice = [&](int sl, int t, bool first) {
+    if constexpr (kFused) {
+      const int64_t k0 = (int64_t)sl * kSliceBits;
+      const int64_t kend = k0 + kSliceBits < K ? k0 + kSliceBits : K;
+      const int64_t g_lo = k0 / li.D;
+      const int64_t c_lo = g_lo * li.d;
+      const int64_t c_hi = ((kend - 1) / li.D + 1) * li.d;
+      const int nch = static_cast<int>(c_hi - c_lo);
+      const int sub = tid & 7;                  // 16 of the row's 128 terms
+      const int npass = (nch + 127) / 128;
+      bool issued = !first;
+      constexpr int kP = LDT == LQ_F32 ? 1 : 3;  // passes in flight
+      for (int p0 = 0; p0 < npass; p0 += kP) {
+        uint4 tv[kP][4], av[kP][4];
+#pragma unroll
+        for (int u = 0; u < kP; ++u) {
+          const int ci = (p0 + u) * 128 + (tid >> 3);
+          if (p0 + u < npass && ci < nch) {
+            const int64_t c = c_lo + ci;
+            const int64_t q = c >> 7;
+            load16raw<LDT>(li.t, (q * 128 + (c & 127)) * 128 + 16 * sub, tv[u]);
+            load16raw<LDT>(li.a, q * 128 + 16 * sub, av[u]);
+          }
+        }
+        if (!issued) {
+          ld_next_slice();
+          issue(wb[0]);
+          issue(wb[1]);
+          issued = true;
+        }
+#pragma unroll
+        for (int u = 0; u < kP; ++u) {
+          const int ci = (p0 + u) * 128 + (tid >> 3);
+          float acc = 0.f;
+          if (p0 + u < npass && ci < nch) {
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+              acc = fmaf(raw_elem<LDT>(tv[u], k), raw_elem<LDT>(av[u], k), acc);
+          }
+          acc = sum8(acc);
+          if (p0 + u < npass && ci < nch && sub == 0) ul[ci] = acc;
+        }
+      }
+      __syncthreads();                          // u complete; xs of the last tables read
+      {
+        const int64_t k = k0 + tid;
+        float v = 0.f;
+        if (k < kend) {
+          const int64_t g = k / li.D;
+          const int j = static_cast<int>(k - g * li.D);
+          const float* ur = ul + (g * li.d - c_lo);
+          for (int r2 = 0; r2 < li.d; ++r2) v = fmaf(li.M[r2 * li.D + j], ur[r2], v);
+        }
+        xs[t * kSliceBits + tid] = v;
+      }
+      __syncthreads();                          // xs complete; ul free again
+    }
+  };
   auto tables = [&](int sp, bool first) {
     const int nt = sp + 1 <= sl_last ? 2 : 1;
     float4 xa[2][4];
+    if constexpr (kFused) {
+      // every wave is past its lookups of the old tables once it reaches the
+      // lift's first barrier
+      lift_slice(sp, 0, first);
+      if (nt == 2) lift_slice(sp + 1, 1, false);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (t < nt) {
-        load_x(ares, K, 0, sp + t, h_pos(2 * lane), xa[t][0], xa[t][1]);
-        load_x(ares, K, 0, sp + t, h_pos(2 * lane + 1), xa[t][2], xa[t][3]);
+      for (int t = 0; t < 2; ++t) {
+        if (t < nt) {
+          const float4* x4 = reinterpret_cast<const float4*>(xs + t * kSliceBits);
+          xa[t][0] = x4[2 * h_pos(2 * lane)];
+          xa[t][1] = x4[2 * h_pos(2 * lane) + 1];
+          xa[t][2] = x4[2 * h_pos(2 * lane + 1)];
+          xa[t][3] = x4[2 * h_pos(2 * lane + 1) + 1];
+        }
       }
-    }
-    __syncthreads();                            // activations requested before any weight;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        if (t < nt) {
+          load_x(ares, K, 0, sp + t, h_pos(2 * lane), xa[t][0], xa[t][1]);
+          load_x(ares, K, 0, sp + t, h_pos(2 * lane + 1), xa[t][2], xa[t][3]);
+        }
+      }
+      __syncthreads();                          // activations requested before any weight;
                                                 // nobody reads the old tables any more
-    if (first) {
-      ld_next_slice();
-      issue(wb[0]);
-      issue(wb[1]);
+      if (first) {
+        ld_next_slice();
+        issue(wb[0]);
+        issue(wb[1]);
+      }
     }
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -499,7 +632,57 @@ Sched1 make_sched1(int64_t m, int64_t K) {
   return sc;
 }
 
+template <int P>
+static void launch_reduce(const float* partials, const float* s, float* out, int64_t m, int S,
+                          hipStream_t st);
+
+void reduce_slices(const float* partials, const float* s, float* out, int64_t m, int S,
+                   hipStream_t st) {
+  const int need = (S + 7) / 8;                 // parts so that each adds <= 8 slices
+  if (need <= 1)
+    launch_reduce<1>(partials, s, out, m, S, st);
+  else if (need <= 2)
+    launch_reduce<2>(partials, s, out, m, S, st);
+  else if (need <= 4)
+    launch_reduce<4>(partials, s, out, m, S, st);
+  else if (need <= 8)
+    launch_reduce<8>(partials, s, out, m, S, st);
+  else
+    launch_reduce<16>(partials, s, out, m, S, st);
+}
+
+template <int LDT>
+hipError_t launch_fused(const LiftIn& li, const uint32_t* w, int64_t m, int64_t K, int64_t ldw,
+                        const float* s, float* out, void* ws, hipStream_t st) {
+  const Sched1 sc = make_sched1(m, K);
+  const uint32_t w_bytes = static_cast<uint32_t>(m * ldw * 4);
+  const uint32_t a_bytes = static_cast<uint32_t>(K * 4);
+  if (sc.S == 1) {
+    hipLaunchKernelGGL((gemv1_kernel<false, LDT>), dim3(sc.G), dim3(kThreads), 0, st, w, m, K,
+                       ldw, s, nullptr, out, nullptr, sc, w_bytes, a_bytes, li);
+    return hipGetLastError();
+  }
+  float* partials = static_cast<float*>(ws);
+  hipLaunchKernelGGL((gemv1_kernel<true, LDT>), dim3(sc.G), dim3(kThreads), 0, st, w, m, K, ldw,
+                     s, nullptr, out, partials, sc, w_bytes, a_bytes, li);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  reduce_slices(partials, s, out, m, sc.S, st);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_layer_b1(const void* a, lq_dtype dt, const void* t_inv, const float* M, int d,
+                           int D, const uint32_t* w, int64_t m, int64_t K, int64_t ldw,
+                           const float* s, float* out, void* ws, hipStream_t st) {
+  const LiftIn li{a, t_inv, M, d, D};
+  switch (dt) {
+    case LQ_F32: return launch_fused<LQ_F32>(li, w, m, K, ldw, s, out, ws, st);
+    case LQ_F16: return launch_fused<LQ_F16>(li, w, m, K, ldw, s, out, ws, st);
+    default: return launch_fused<LQ_BF16>(li, w, m, K, ldw, s, out, ws, st);
+  }
+}
 
 size_t gemv1_workspace_bytes(int64_t m, int64_t K) {
   const Sched1 sc = make_sched1(m, K);
@@ -514,25 +697,15 @@ hipError_t launch_gemv1(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, co
   const uint32_t w_bytes = static_cast<uint32_t>(m * ldw * 4);
   const uint32_t a_bytes = static_cast<uint32_t>(K * 4);
   if (sc.S == 1) {
-    hipLaunchKernelGGL(gemv1_kernel<false>, dim3(sc.G), dim3(kThreads), 0, st, w, m, K, ldw, s,
-                       a_lift, out, nullptr, sc, w_bytes, a_bytes);
+    hipLaunchKernelGGL((gemv1_kernel<false, -1>), dim3(sc.G), dim3(kThreads), 0, st, w, m, K,
+                       ldw, s, a_lift, out, nullptr, sc, w_bytes, a_bytes, LiftIn{});
   } else {
     float* partials = static_cast<float*>(ws);
-    hipLaunchKernelGGL(gemv1_kernel<true>, dim3(sc.G), dim3(kThreads), 0, st, w, m, K, ldw, s,
-                       a_lift, out, partials, sc, w_bytes, a_bytes);
+    hipLaunchKernelGGL((gemv1_kernel<true, -1>), dim3(sc.G), dim3(kThreads), 0, st, w, m, K,
+                       ldw, s, a_lift, out, partials, sc, w_bytes, a_bytes, LiftIn{});
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int need = (sc.S + 7) / 8;            // parts so that each adds <= 8 slices
-    if (need <= 1)
-      launch_reduce<1>(partials, s, out, m, sc.S, st);
-    else if (need <= 2)
-      launch_reduce<2>(partials, s, out, m, sc.S, st);
-    else if (need <= 4)
-      launch_reduce<4>(partials, s, out, m, sc.S, st);
-    else if (need <= 8)
-      launch_reduce<8>(partials, s, out, m, sc.S, st);
-    else
-      launch_reduce<16>(partials, s, out, m, sc.S, st);
+    reduce_slices(partials, s, out, m, sc.S, st);
   }
   return hipGetLastError();
 }

@@ -321,6 +321,56 @@ lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw, c
                     "lq_gemv launch");
 }
 
+lq_status lq_layer_b1_workspace_size(int64_t m, int64_t n, int32_t d, int32_t D,
+                                     size_t* bytes) {
+  if (!bytes) return fail(LQ_ERR_NULL, "bytes is null");
+  if (m < 1 || n < 1 || d < 1 || D < 1 || n % d)
+    return fail(LQ_ERR_SHAPE, "m=%lld n=%lld d=%d D=%d", (long long)m, (long long)n, (int)d,
+                (int)D);
+  *bytes = lq::gemv1_workspace_bytes(m, n / d * D);
+  return ok();
+}
+
+lq_status lq_layer_b1(const void* a, lq_dtype a_dtype, int64_t n, const void* t_inv,
+                      lq_dtype t_dtype, int32_t t_block, const float* M, int32_t d, int32_t D,
+                      const uint32_t* w_packed, int64_t m, int64_t ldw, const float* s,
+                      float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!a || !t_inv || !M || !w_packed || !s || !out) return fail(LQ_ERR_NULL, "null pointer");
+  if (!valid_dtype(a_dtype) || a_dtype != t_dtype)
+    return fail(LQ_ERR_DTYPE, "a and t_inv must share one of LQ_F16, LQ_BF16, LQ_F32");
+  if (t_block != 128)
+    return fail(LQ_ERR_UNSUPPORTED, "t_block=%d (only 128 is implemented)", (int)t_block);
+  if (m < 1 || n < 1 || n % 128 || d < 1 || d > 64 || D > 256 || d * D > 8192 || n % d)
+    return fail(LQ_ERR_SHAPE, "m=%lld n=%lld d=%d D=%d (n %% 128 == 0, n %% d == 0, 1 <= d <= "
+                "64, D <= 256, d*D <= 8192)", (long long)m, (long long)n, (int)d, (int)D);
+  if (D < d)
+    return fail(LQ_ERR_UNSUPPORTED, "D=%d < d=%d (below one bit per weight) is not fused",
+                (int)D, (int)d);
+  const int64_t K = n / d * D;
+  if (ldw < (K + 31) / 32) return fail(LQ_ERR_SHAPE, "ldw=%lld < ceil(K/32)", (long long)ldw);
+  if (ldw % 4) return fail(LQ_ERR_ALIGN, "ldw=%lld must be a multiple of 4", (long long)ldw);
+  if (K % 4) return fail(LQ_ERR_SHAPE, "K=%lld must be a multiple of 4", (long long)K);
+  if (m * ldw * 4 > ((int64_t)1 << 30))
+    return fail(LQ_ERR_SHAPE, "weights of %lld bytes exceed the 1 GiB per-call limit",
+                (long long)(m * ldw * 4));
+  if (K > ((int64_t)1 << 24))
+    return fail(LQ_ERR_SHAPE, "K=%lld exceeds the per-call limit of 2^24", (long long)K);
+  if (!aligned(w_packed, 16) || !aligned(a, 16) || !aligned(t_inv, 16))
+    return fail(LQ_ERR_ALIGN, "w_packed, a and t_inv must be 16-byte aligned");
+  if (!aligned(M, 4) || !aligned(s, 4) || !aligned(out, 4))
+    return fail(LQ_ERR_ALIGN, "misaligned M, s or out");
+  const size_t need = lq::gemv1_workspace_bytes(m, K);
+  if (need > 0) {
+    if (!workspace) return fail(LQ_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+    if (workspace_bytes < need)
+      return fail(LQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    if (!aligned(workspace, 256)) return fail(LQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+  }
+  return hip_status(lq::launch_layer_b1(a, a_dtype, t_inv, M, d, D, w_packed, m, K, ldw, s, out,
+                                        workspace, as_stream(stream)),
+                    "lq_layer_b1 launch");
+}
+
 lq_status lq_gemm(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw, const float* s,
                   const void* a_lift, lq_dtype lift_dtype, int64_t B, float* out, void* stream) {
   if (!w_packed || !s || !a_lift || !out) return fail(LQ_ERR_NULL, "null pointer");

@@ -118,6 +118,10 @@ int num_cus();
 
 // One-token GEMV on float16 activation-sum tables (k_gemv1.hip).
 size_t gemv1_workspace_bytes(int64_t m, int64_t K);
+// One-token layer with the lift in the GEMV's table prologue (k_gemv1.hip).
+hipError_t launch_layer_b1(const void* a, lq_dtype dt, const void* t_inv, const float* M, int d,
+                           int D, const uint32_t* w, int64_t m, int64_t K, int64_t ldw,
+                           const float* s, float* out, void* ws, hipStream_t st);
 hipError_t launch_gemv1(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
                         const float* a_lift, float* out, void* ws, hipStream_t st);
 

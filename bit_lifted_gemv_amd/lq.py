@@ -28,7 +28,7 @@ EXPORTS = ("lq_status_string", "lq_last_error", "lq_version", "lq_pack_signs", "
            "lq_gemv_workspace_size", "lq_workspace_clear", "lq_gemv", "lq_gemm",
            "lq_encode_workspace_size", "lq_encode", "lq_softmin_workspace_size",
            "lq_softmin_grad", "lq_adam_update", "lq_gemm_decoded_workspace_size",
-           "lq_gemm_decoded")
+           "lq_gemm_decoded", "lq_layer_b1_workspace_size", "lq_layer_b1")
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -65,6 +65,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lq_encode": (_i32, [_vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
         "lq_softmin_workspace_size": (_i32, [_i64, _i32, _i32, ctypes.POINTER(_sz)]),
         "lq_gemm_decoded_workspace_size": (_i32, [_i64, _i64, ctypes.POINTER(_sz)]),
+        "lq_layer_b1_workspace_size": (_i32, [_i64, _i64, _i32, _i32, ctypes.POINTER(_sz)]),
+        "lq_layer_b1": (_i32, [_vp, _i32, _i64, _vp, _i32, _i32, _vp, _i32, _i32, _vp, _i64, _i64,
+                               _vp, _vp, _vp, _sz, _vp]),
         "lq_gemm_decoded": (_i32, [_vp, _i64, _i64, _i64, _vp, _i32, _i32, _vp, _vp, _i32, _i64,
                                    _vp, _vp, _sz, _vp]),
         "lq_softmin_grad": (_i32, [_vp, _i64, _vp, _i32, _i32, ctypes.c_float, _vp, _vp, _vp,
@@ -207,6 +210,25 @@ def encode(w: torch.Tensor, M: torch.Tensor, A: Optional[torch.Tensor] = None,
     return codes, err
 
 
+def layer_b1(a: torch.Tensor, t_inv: torch.Tensor, M: torch.Tensor, d: int, D: int,
+             w_packed: torch.Tensor, s: torch.Tensor, out: Optional[torch.Tensor] = None,
+             stream=None) -> torch.Tensor:
+    """The whole layer for one token (a [n] or [1][n]): lift inside the
+    one-token product; out float32 [1][m]."""
+    _dev(a, t_inv, M, w_packed, s)
+    n = a.shape[-1]
+    m, ldw = w_packed.shape
+    if out is None:
+        out = torch.empty((1, m), dtype=torch.float32, device=a.device)
+    nb = _sz(0)
+    check(lib().lq_layer_b1_workspace_size(m, n, d, D, ctypes.byref(nb)))
+    ws = workspace(nb.value, a.device, m) if nb.value else None
+    check(lib().lq_layer_b1(_ptr(a), _dt(a), n, _ptr(t_inv), _dt(t_inv), 128, _ptr(M), d, D,
+                            _ptr(w_packed), m, ldw, _ptr(s), _ptr(out), _ptr(ws), nb.value,
+                            _stream(stream)))
+    return out
+
+
 def gemm_decoded(w_packed: torch.Tensor, s: torch.Tensor, M: torch.Tensor, d: int, D: int,
                  u: torch.Tensor, out: Optional[torch.Tensor] = None,
                  stream=None) -> torch.Tensor:
@@ -346,10 +368,14 @@ class DeviceLayer:
 
     def forward(self, a: torch.Tensor, gemm_dtype: torch.dtype = torch.float16,
                 path: str = "auto") -> torch.Tensor:
-        """o [B][m]: lift then the GEMV (B <= 16) or the GEMM (larger B); with
-        path "decoded", u = T^-1 a (the lift with M = I_4) then the
+        """o [B][m]: lift then the GEMV (B <= 16) or the GEMM (larger B), the
+        faster paths at the workload shapes.  Paths: "gemv" / "gemm" force
+        those; "fused" the one-token layer with the lift inside the GEMV
+        (lq_layer_b1); "decoded" u = T^-1 a (the lift with M = I_4) then the
         decode-weights product."""
         B = a.shape[0]
+        if path == "fused":
+            return layer_b1(a, self.t_inv, self.M, self.d, self.D, self.w, self.s)
         if path == "decoded":
             eye = torch.eye(4, dtype=torch.float32, device=a.device)
             u = lift(a, self.t_inv, eye, 4, 4, out_dtype=torch.float16)

@@ -277,6 +277,35 @@ lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * lq_layer_b1 -- the whole layer for one token, o = diag(s) W_q lift(T^-1 a)
+ * (关键设计 4), with the lift computed inside the one-token product: each
+ * workgroup of the weight stream computes the lifted activations of the
+ * 1024-position slices its tables serve (u = T^-1 a for the slices'
+ * channels, then a_hat_g = M^T u_g, float32) before building the tables,
+ * while its first weights stream in.  No a_hat buffer, no lift launch; the
+ * result is lq_lift_activations followed by lq_gemv with B == 1 (same table
+ * arithmetic, a_hat summed in another order).
+ * a:      [n] of a_dtype;  t_inv: [n/128][128][128] of t_dtype == a_dtype
+ *         (LQ_F16, LQ_BF16 or LQ_F32), both 16-byte aligned;  t_block: 128.
+ * M:      float [d][D];  w_packed: uint32 [m][ldw] (lq_pack_signs layout),
+ *         ldw >= ceil(K/32), a multiple of 4, 16-byte aligned, K = n*D/d.
+ * s:      float [m];  out: float [m].
+ * workspace: >= lq_layer_b1_workspace_size bytes (0 when K <= 1024),
+ *         256-byte aligned, caller-owned, no initialisation needed.
+ * Requires n % 128 == 0, n % d == 0, 1 <= d <= D <= 256, d <= 64,
+ * d*D <= 8192, K % 4 == 0, K <= 2^24, m*ldw*4 <= 2^30 (else LQ_ERR_SHAPE,
+ * LQ_ERR_UNSUPPORTED or LQ_ERR_ALIGN; nothing launched).  Arithmetic as
+ * lq_gemv with B == 1 (float16 activation-sum tables, exact power-of-two
+ * scaling, float32 sums).
+ */
+lq_status lq_layer_b1_workspace_size(int64_t m, int64_t n, int32_t d, int32_t D,
+                                     size_t* bytes);
+lq_status lq_layer_b1(const void* a, lq_dtype a_dtype, int64_t n, const void* t_inv,
+                      lq_dtype t_dtype, int32_t t_block, const float* M, int32_t d, int32_t D,
+                      const uint32_t* w_packed, int64_t m, int64_t ldw, const float* s,
+                      float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * lq_gemm -- the same product for large batches, contracted on the matrix
  * cores: out[b][i] = s[i] * sum_k sigma_ik * a_lift[b][k] with a_lift in
  * 16-bit (LQ_F16 or LQ_BF16) [B][K]; signs are expanded to exact +-1 16-bit

@@ -201,6 +201,30 @@ def test_gemm_decoded_validation(L):
     assert call(u=P + 1) == 4
 
 
+def test_layer_b1_validation(L):
+    nb = ctypes.c_size_t(0)
+    assert L.lq_layer_b1_workspace_size(28672, 8192, 8, 19, ctypes.byref(nb)) == 0
+    assert nb.value > 0
+    assert L.lq_layer_b1_workspace_size(64, 256, 4, 4, ctypes.byref(nb)) == 0
+    assert nb.value == 0                      # one slice: no partial sums
+    BF16, F16 = lq.LQ_BF16, lq.LQ_F16
+
+    def call(a=P, adt=BF16, n=8192, t=P, tdt=BF16, tb=128, M=P, d=8, D=19, w=P, m=64,
+             ldw=608, s=P, out=P, ws=P, wsb=1 << 24):
+        return L.lq_layer_b1(a, adt, n, t, tdt, tb, M, d, D, w, m, ldw, s, out, ws, wsb, None)
+
+    assert call(a=None) == 1
+    assert call(tdt=F16) == 3                 # a and t_inv differ
+    assert call(tb=64) == 5
+    assert call(n=8000) == 2                  # n % 128
+    assert call(d=16, D=8, ldw=128) == 5      # below one bit per weight
+    assert call(ldw=600) == 2                 # ldw < ceil(K/32) = 608
+    assert call(ldw=610) == 4                 # ldw % 4
+    assert call(a=P + 8) == 4
+    assert call(wsb=16) == 7
+    assert call(ws=P + 16) == 4
+
+
 def test_gemm_and_pack_validation(L):
     assert L.lq_gemm(P, 8, 64, 2, P, P, lq.LQ_F32, 512, P, None) == 3       # f32 activations
     assert L.lq_gemm(P, 8, 60, 2, P, P, lq.LQ_F16, 512, P, None) == 2       # K % 8

@@ -372,3 +372,29 @@ def test_full_size_case(dev, cfg, si, shape, B):
     _banner(f"  rel err {e:.3e}")
     assert e <= TOL, e
     assert np.isfinite(got).all()
+
+
+FUSED_CASES = [  # (m, n, d, D, dtype): groups straddling 128-blocks (d = 10), one
+    # slice (K <= 1024: no reduction), d = D, d = 64 (the most channels behind
+    # a slice), float32 and float16 inputs, ragged rows
+    (130, 1280, 10, 24, "f16"), (257, 1024, 8, 20, "bf16"), (96, 2048, 8, 16, "bf16"),
+    (64, 384, 3, 7, "bf16"), (33, 256, 4, 4, "bf16"), (50, 4096, 8, 8, "f16"),
+    (70, 1280, 64, 64, "bf16"), (41, 1024, 16, 40, "f32"), (300, 8192, 8, 19, "bf16"),
+]
+
+
+@pytest.mark.parametrize("m,n,d,D,dt", FUSED_CASES)
+def test_layer_b1_fused(dev, m, n, d, D, dt):
+    """The one-token layer with the lift inside the GEMV against the oracle,
+    and against the unfused path (lift, then the GEMV) on the same inputs."""
+    _banner(f"fused layer m={m} n={n} D/d={D}/{d} {dt}")
+    L = synth.make_layer(m, n, d, D, 1, seed=m + n + d, dtype=dt, outlier_frac=0.01)
+    ref = O.forward(L.packed, L.K, L.M, L.t_inv, L.s, L.a, d, D, dt)
+    dl = lq.DeviceLayer.from_synth(L, device=dev)
+    a = _up(L.a, dt, dev)
+    fused = dl.forward(a, path="fused").cpu().numpy()
+    split = dl.forward(a, path="gemv").cpu().numpy()
+    e = O.rel_err_colmax(fused, ref)
+    _banner(f"  rel err {e:.3e}  vs unfused {O.rel_err_colmax(fused, split):.3e}")
+    assert e <= TOL_LUT16, e
+    assert O.rel_err_colmax(fused, split) <= TOL_LUT16
