@@ -26,7 +26,9 @@
 //   bwd: lane = code t, workgroup = 256 codes x one slice of the samples
 //     (staged in LDS, read as broadcasts); accumulates beta_t and
 //     sum_n b_nt w_n, then sums 2T (sum b w - beta C_t) y_t^T over its codes.
-//   reduce: one workgroup adds the partial sums in a fixed order.
+//   reduce: the forward and backward partial rows are added column-wise by
+//     a fixed tree (16 rows per node, consecutive rows, left to right),
+//     then one small kernel forms the loss and the gradient.
 // Everything is deterministic (fixed partition, fixed summation order).
 #include <cmath>
 
@@ -320,23 +322,36 @@ __global__ void __launch_bounds__(kT) softmin_bwd_kernel(
                                       (d * D));
 }
 
-__global__ void __launch_bounds__(kT) softmin_reduce_kernel(const float* __restrict__ fpart,
-                                                            int nf, const float* __restrict__ bpart,
-                                                            int nb, int dD, float inv_n,
-                                                            float* __restrict__ loss,
-                                                            float* __restrict__ grad) {
-  for (int e = threadIdx.x; e < dD; e += kT) {
-    float s = 0.f;
-    for (int i = 0; i < nf; ++i) s += fpart[static_cast<int64_t>(i) * (1 + dD) + 1 + e];
-    float sbk = 0.f;
-    for (int i = 0; i < nb; ++i) sbk += bpart[static_cast<int64_t>(i) * dD + e];
-    grad[e] = (s + sbk) * inv_n;
-  }
-  if (threadIdx.x == 0) {
-    float s = 0.f;
-    for (int i = 0; i < nf; ++i) s += fpart[static_cast<int64_t>(i) * (1 + dD)];
-    *loss = s * inv_n;
-  }
+constexpr int kFan = 16;   // rows added per node of the reduction tree
+
+// out[c][e] = in[kFan c][e] + ... + in[kFan c + kFan - 1][e] (rows past nrows
+// count as absent), added left to right.  Row c of the output per blockIdx.x,
+// columns in blocks of kT per blockIdx.y; all of a lane's loads are issued
+// before the first add.
+__global__ void __launch_bounds__(kT) softmin_sum_rows_kernel(const float* __restrict__ in,
+                                                              int nrows, int ncols,
+                                                              float* __restrict__ out) {
+  const int e = blockIdx.y * kT + threadIdx.x;
+  if (e >= ncols) return;
+  const int r0 = blockIdx.x * kFan;
+  float v[kFan];
+#pragma unroll
+  for (int u = 0; u < kFan; ++u)
+    v[u] = r0 + u < nrows ? in[static_cast<int64_t>(r0 + u) * ncols + e] : 0.f;
+  float sum = v[0];
+#pragma unroll
+  for (int u = 1; u < kFan; ++u) sum += v[u];
+  out[static_cast<int64_t>(blockIdx.x) * ncols + e] = sum;
+}
+
+// f: the summed forward row (loss, then d D gradient terms); b: the summed
+// backward row (d D terms).
+__global__ void __launch_bounds__(kT) softmin_final_kernel(const float* __restrict__ f,
+                                                           const float* __restrict__ b, int dD,
+                                                           float inv_n, float* __restrict__ loss,
+                                                           float* __restrict__ grad) {
+  for (int e = threadIdx.x; e < dD; e += kT) grad[e] = (f[1 + e] + b[e]) * inv_n;
+  if (threadIdx.x == 0) *loss = f[0] * inv_n;
 }
 
 __global__ void __launch_bounds__(kT) adam_kernel(float* __restrict__ M,
@@ -381,8 +396,32 @@ Plan plan(int64_t N, int D) {
 }
 
 struct Layout {
-  size_t part, samp, fpart, bpart, total;   // float offsets
+  size_t part, samp, fpart, bpart, ftree, btree, total;   // float offsets
 };
+
+// Floats of the two ping-pong buffers of a reduction of `rows` rows of
+// `cols`: the first level's output and the second's.
+size_t tree_floats(size_t rows, size_t cols) {
+  const size_t l1 = (rows + kFan - 1) / kFan;
+  const size_t l2 = (l1 + kFan - 1) / kFan;
+  return (l1 + l2) * cols;
+}
+
+// Adds the rows of `in` column-wise, kFan rows per node, until one row
+// remains; returns it (in `in` itself when rows == 1, else in `tree`).
+const float* reduce_rows(const float* in, int rows, int cols, float* tree, hipStream_t st) {
+  float* buf[2] = {tree, tree + static_cast<size_t>((rows + kFan - 1) / kFan) * cols};
+  int k = 0;
+  while (rows > 1) {
+    const int out_rows = (rows + kFan - 1) / kFan;
+    hipLaunchKernelGGL(softmin_sum_rows_kernel, dim3(out_rows, (cols + kT - 1) / kT), dim3(kT),
+                       0, st, in, rows, cols, buf[k]);
+    in = buf[k];
+    k ^= 1;
+    rows = out_rows;
+  }
+  return in;
+}
 
 Layout layout(int64_t N, int d, int D) {
   const Plan p = plan(N, D);
@@ -392,7 +431,9 @@ Layout layout(int64_t N, int d, int D) {
   l.samp = up(static_cast<size_t>(p.S) * N * (D + 2));
   l.fpart = l.samp + up(static_cast<size_t>(N) * (D + 3));
   l.bpart = l.fpart + up(static_cast<size_t>(p.nfw) * (1 + d * D));
-  l.total = l.bpart + up(static_cast<size_t>(p.nbx) * p.nby * d * D);
+  l.ftree = l.bpart + up(static_cast<size_t>(p.nbx) * p.nby * d * D);
+  l.btree = l.ftree + up(tree_floats(p.nfw, 1 + d * D));
+  l.total = l.btree + up(tree_floats(static_cast<size_t>(p.nbx) * p.nby, d * D));
   return l;
 }
 
@@ -407,8 +448,10 @@ hipError_t launch_dm(const float* W, int N, const float* M, int d, int D, float 
                      d, D, T, p.S, ws + l.part, ws + l.samp, ws + l.fpart);
   hipLaunchKernelGGL((softmin_bwd_kernel<DM, XM>), dim3(p.nbx, p.nby), dim3(kT), 0, st, W, N, M,
                      d, D, T, p.n_slice, ws + l.samp, ws + l.bpart);
-  hipLaunchKernelGGL(softmin_reduce_kernel, dim3(1), dim3(kT), 0, st, ws + l.fpart, p.nfw,
-                     ws + l.bpart, p.nbx * p.nby, d * D, 1.f / static_cast<float>(N), loss, grad);
+  const float* f = reduce_rows(ws + l.fpart, p.nfw, 1 + d * D, ws + l.ftree, st);
+  const float* b = reduce_rows(ws + l.bpart, p.nbx * p.nby, d * D, ws + l.btree, st);
+  hipLaunchKernelGGL(softmin_final_kernel, dim3(1), dim3(kT), 0, st, f, b, d * D,
+                     1.f / static_cast<float>(N), loss, grad);
   return hipGetLastError();
 }
 
