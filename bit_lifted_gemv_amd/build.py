@@ -25,9 +25,6 @@ HIPCC_FLAGS = [
     "-Wno-unused-function",
     # packed fp32 instructions are kept out of the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # one lane issues each arrival-counter increment; the wave-wide atomic
-    # rewrite would wait for the result at once and drain the load stream
-    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
 ]
 
 
