@@ -194,6 +194,33 @@ def test_gemv_lifted_product(dev, m, K, B):
     assert e <= (TOL_LUT16 if B == 1 else TOL_F32), e
 
 
+@pytest.mark.parametrize("B", [1, 3])
+def test_gemv_largest_weight_buffer(dev, B):
+    """The largest weight matrix one call accepts, m * ldw * 4 = 2^30 bytes
+    (4096 rows of 2^21 lifted positions: 32-bit buffer offsets up to their
+    limit, 2048 slices for one token), checked on sampled rows.  The signs
+    are drawn on the device by torch's seeded generator."""
+    _banner(f"gemv largest weights 4096 x 2^21 B={B}")
+    m, K = 4096, 1 << 21
+    ldw = K // 32
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77 + B)
+    w = torch.randint(-(1 << 31), 1 << 31, (m, ldw), dtype=torch.int64, device=dev,
+                      generator=gen).to(torch.int32)
+    rng = np.random.default_rng(78 + B)
+    al = rng.standard_normal((B, K)).astype(np.float32)
+    s = rng.uniform(0.01, 0.03, m).astype(np.float32)
+    got = lq.gemv(w, torch.from_numpy(s).to(dev), torch.from_numpy(al).to(dev), K).cpu().numpy()
+    rows = np.unique(np.concatenate([np.arange(3), np.arange(m - 3, m),
+                                     rng.choice(m, size=6, replace=False)]))
+    packed = w[torch.from_numpy(rows).to(dev)].cpu().numpy().view(np.uint32)
+    ref = O.lifted_product(packed, K, al, s[rows])
+    e = O.rel_err_colmax(got[:, rows], ref)
+    _banner(f"  rel err {e:.3e}")
+    assert e <= (TOL_LUT16 if B == 1 else TOL_F32), e
+    assert np.isfinite(got).all()
+
+
 def test_gemv_deterministic(dev):
     rng = np.random.default_rng(1)
     m, K = 3000, 19456
