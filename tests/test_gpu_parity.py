@@ -321,6 +321,52 @@ def test_gemm_lifted_product(dev, m, K, B, pad, odt):
     assert e <= 1e-4, e   # operands are exact; float32 accumulation only
 
 
+def test_gemm_longest_lifted_dimension(dev):
+    """K = 2^22 (the largest lifted dimension lq_gemm accepts: 16384 steps of
+    256 positions), two row tiles and one token tile, checked on sampled rows
+    against the oracle.  Signs and activations are drawn on the device by
+    torch's seeded generator."""
+    _banner("gemm K = 2^22")
+    m, K, B = 160, 1 << 22, 16
+    ldw = K // 32
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(91)
+    w = torch.randint(-(1 << 31), 1 << 31, (m, ldw), dtype=torch.int64, device=dev,
+                      generator=gen).to(torch.int32)
+    al = torch.randn((B, K), device=dev, generator=gen).to(torch.float16)
+    s = torch.rand(m, device=dev, generator=gen) * 0.02 + 0.01
+    got = lq.gemm(w, s, al, K).cpu().numpy()
+    rows = np.array([0, 1, 127, 128, 129, 158, 159])
+    packed = w[torch.from_numpy(rows).to(dev)].cpu().numpy().view(np.uint32)
+    ref = O.lifted_product(packed, K, al.float().cpu().numpy(), s.cpu().numpy()[rows])
+    e = O.rel_err_colmax(got[:, rows], ref)
+    _banner(f"  rel err {e:.3e}")
+    assert e <= 1e-4, e   # operands are exact; float32 accumulation only
+
+
+def test_gemm_widest_row_stride(dev):
+    """ldw = 2^22 words (the largest row stride lq_gemm accepts: the 128 rows
+    of a tile span 2^31 bytes, the top of the 32-bit buffer range), a short
+    K and garbage in every padding word, two row tiles and a ragged token
+    tile, checked on sampled rows against the oracle."""
+    _banner("gemm ldw = 2^22")
+    m, K, B = 130, 512, 40
+    ldw = 1 << 22
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(93)
+    w = torch.randint(-(1 << 31), 1 << 31, (m, ldw), dtype=torch.int64, device=dev,
+                      generator=gen).to(torch.int32)
+    al = torch.randn((B, K), device=dev, generator=gen).to(torch.bfloat16)
+    s = torch.rand(m, device=dev, generator=gen) * 0.02 + 0.01
+    got = lq.gemm(w, s, al, K).cpu().numpy()
+    rows = np.array([0, 63, 127, 128, 129])
+    packed = w[torch.from_numpy(rows).to(dev), : K // 32].cpu().numpy().view(np.uint32)
+    ref = O.lifted_product(packed, K, al.float().cpu().numpy(), s.cpu().numpy()[rows])
+    e = O.rel_err_colmax(got[:, rows], ref)
+    _banner(f"  rel err {e:.3e}")
+    assert e <= 1e-4, e
+
+
 def test_gemm_one_hot_unpacks_signs_exactly(dev):
     """D = d, M = I, T^-1 = I, s = 1, tokens = identity columns: the GEMM
     output is the +-1 sign matrix itself, bit for bit."""
