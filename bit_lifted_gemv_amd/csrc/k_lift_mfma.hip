@@ -16,8 +16,12 @@
 // a lane takes whole groups of one token (consecutive lanes, consecutive
 // groups, so the writes of a_hat are contiguous) and multiplies its d values
 // of u by M, read 8 columns at a time as scalars (the same for every lane);
-// a last chunk of fewer than 8 columns reads a zero-padded copy in LDS.  Used when 128 % d == 0, so no group
-// straddles two blocks.
+// a last chunk of fewer than 8 columns reads a zero-padded copy in LDS.
+// When D % 8 != 0 a lane's run of D values cannot be written as 16-byte
+// vectors; then, if the workgroup's slab of a_hat (32 tokens x 128 D / d
+// values) fits in LDS beside the rest and its rows are 16-byte aligned, the
+// lanes write it there and the workgroup stores it to memory in whole
+// 16-byte pieces of consecutive addresses.  Used when 128 % d == 0, so no group straddles two blocks.
 #include "lq_internal.h"
 
 namespace lq {
@@ -105,17 +109,24 @@ __device__ __forceinline__ void store8<LQ_BF16>(void* out, int64_t idx, const fl
   store8_16<LQ_BF16>(out, idx, v, vec, cnt);
 }
 
+// Bytes of dynamic LDS before the staged a_hat slab: M as [d][Dpad] floats.
+__host__ __device__ constexpr int m_lds_bytes(int d, int D) { return (d * ((D + 7) & ~7) * 4 + 15) & ~15; }
+
 // DT: type of a and T^-1 (LQ_F16 or LQ_BF16); O_DT: type of a_hat; DD = d.
 // vec: D % 8 == 0 and out 16-byte aligned (every 8-value run of a_hat then
-// starts 16-byte aligned).
+// starts 16-byte aligned).  staged: the slab goes through LDS (see above).
 template <int DT, int O_DT, int DD>
 __global__ void __launch_bounds__(kThreads) lift_mfma_kernel(
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ t_inv,
-    const float* __restrict__ M, void* __restrict__ out, int B, int n, int D, int K, bool vec) {
+    const float* __restrict__ M, void* __restrict__ out, int B, int n, int D, int K, bool vec,
+    bool staged) {
   __shared__ __attribute__((aligned(16))) float su[kWaves][kTok * kUld];   // 18 KB
-  extern __shared__ float4 sM4[];                 // M, [d][Dpad], zero padded
+  extern __shared__ float4 sM4[];                 // M, [d][Dpad], zero padded; then the slab
   float* sM = reinterpret_cast<float*>(sM4);
   const int Dpad = (D + 7) & ~7;
+  constexpr int kOB = O_DT == LQ_F32 ? 4 : 2;     // bytes per a_hat value
+  const int per_tok = (kTB / DD) * D;             // a_hat values of this workgroup per token
+  char* const slab = reinterpret_cast<char*>(sM4) + m_lds_bytes(DD, D);
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -170,6 +181,7 @@ __global__ void __launch_bounds__(kThreads) lift_mfma_kernel(
   constexpr int kRB = DD < 8 ? DD : 8;
   int ubase[kPC];
   int64_t obase[kPC];
+  int sbase[kPC];
   bool live[kPC];
 #pragma unroll
   for (int pc = 0; pc < kPC; ++pc) {
@@ -177,11 +189,14 @@ __global__ void __launch_bounds__(kThreads) lift_mfma_kernel(
     const int tt = pidx / kGw;
     const int g = pidx - tt * kGw;
     live[pc] = pidx < kPairs && t0 + tt < B;
-    ubase[pc] = tt * kUld + g * DD;
+    ubase[pc] = live[pc] ? tt * kUld + g * DD : 0;
     obase[pc] = static_cast<int64_t>(t0 + tt) * K +
                 static_cast<int64_t>(q * (kTB / DD) + wave * kGw + g) * D;
+    sbase[pc] = tt * per_tok + (wave * kGw + g) * D;
   }
-  if (!live[0]) return;   // later pairs of the lane are dead too; no barrier follows
+  // later pairs of a lane are dead when its first is; without the slab no
+  // barrier follows
+  if (!live[0] && !staged) return;
   // Whole chunks of 8 columns read M from global memory at addresses that are
   // the same for every lane (scalar loads, an SGPR operand per multiply-add);
   // a last chunk of fewer than 8 columns reads the zero-padded copy in LDS.
@@ -224,8 +239,27 @@ __global__ void __launch_bounds__(kThreads) lift_mfma_kernel(
       }
     }
 #pragma unroll
-    for (int pc = 0; pc < kPC; ++pc)
-      if (live[pc]) store8<O_DT>(out, obase[pc] + j0, o[pc], vec, D - j0);
+    for (int pc = 0; pc < kPC; ++pc) {
+      if (!live[pc]) continue;
+      if (staged)
+        store8<O_DT>(slab, sbase[pc] + j0, o[pc], vec, D - j0);
+      else
+        store8<O_DT>(out, obase[pc] + j0, o[pc], vec, D - j0);
+    }
+  }
+  if (staged) {
+    // the slab, row by row (token rows of per_tok values), in 16-byte pieces
+    __syncthreads();
+    const int rows = min(kTok, B - t0);
+    const int cpr = per_tok * kOB / 16;
+    char* const gbase = static_cast<char*>(out) +
+                        (static_cast<int64_t>(t0) * K + static_cast<int64_t>(q) * per_tok) * kOB;
+    for (int i = threadIdx.x; i < rows * cpr; i += kThreads) {
+      const int r = i / cpr;
+      const int c = i - r * cpr;
+      const uint4 v = *reinterpret_cast<const uint4*>(slab + (r * per_tok) * kOB + 16 * c);
+      *reinterpret_cast<uint4*>(gbase + static_cast<int64_t>(r) * K * kOB + 16 * c) = v;
+    }
   }
 }
 
@@ -234,11 +268,26 @@ hipError_t launch_dd(const void* a, int64_t B, int64_t n, const void* t_inv, con
                      int D, void* out, hipStream_t st) {
   const int K = static_cast<int>(n / DD * D);
   const dim3 grid(static_cast<unsigned>(n / kTB), static_cast<unsigned>((B + kTok - 1) / kTok));
-  const size_t lds = sizeof(float) * DD * ((D + 7) & ~7);
+  // The slab goes through LDS when the lanes' own runs cannot be written as
+  // 16-byte vectors (D % 8 != 0: value-by-value stores), the slab's rows and
+  // their places in a_hat are 16-byte aligned, and everything stays within
+  // 64 KB of LDS.  (With 16-byte runs the direct stores measured faster: the
+  // larger LDS footprint costs more resident workgroups than the partly
+  // filled lines cost.)
+  const int ob = O_DT == LQ_F32 ? 4 : 2;
+  const int64_t per_tok = static_cast<int64_t>(kTB / DD) * D;
+  const bool aligned16 = reinterpret_cast<uintptr_t>(out) % 16 == 0;
+  const size_t static_lds = sizeof(float) * kWaves * kTok * kUld;
+  const size_t slab_bytes = static_cast<size_t>(kTok * per_tok * ob);
+  const bool staged = D % 8 != 0 && aligned16 && (per_tok * ob) % 16 == 0 &&
+                      (int64_t{K} * ob) % 16 == 0 &&
+                      static_lds + m_lds_bytes(DD, D) + slab_bytes <= 65536;
+  const size_t lds = m_lds_bytes(DD, D) + (staged ? slab_bytes : 0);
+  // within the slab a lane's 8-value runs are 16-byte aligned when D % 8 == 0
   hipLaunchKernelGGL((lift_mfma_kernel<DT, O_DT, DD>), grid, dim3(kThreads), lds, st,
                      static_cast<const uint16_t*>(a), static_cast<const uint16_t*>(t_inv), M, out,
                      static_cast<int>(B), static_cast<int>(n), D, K,
-                     D % 8 == 0 && reinterpret_cast<uintptr_t>(out) % 16 == 0);
+                     D % 8 == 0 && (staged || aligned16), staged);
   return hipGetLastError();
 }
 
