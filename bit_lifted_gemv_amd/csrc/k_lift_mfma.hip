@@ -315,7 +315,8 @@ hipError_t launch_t(const void* a, int64_t B, int64_t n, const void* t_inv, cons
 }  // namespace
 
 bool lift_mfma_applies(lq_dtype a_dt, lq_dtype t_dt, int64_t B, int64_t n, int d, int D) {
-  return B >= kLiftMfmaMinTokens && a_dt == t_dt && (a_dt == LQ_F16 || a_dt == LQ_BF16) &&
+  const bool enough = B >= 8 || (B >= 4 && n >= 12288);
+  return enough && a_dt == t_dt && (a_dt == LQ_F16 || a_dt == LQ_BF16) &&
          (d == 4 || d == 8 || d == 16 || d == 32) && D <= 256 &&
          static_cast<int64_t>(kTok) * n * 2 < (int64_t{1} << 31);
 }

@@ -79,9 +79,9 @@ hipError_t launch_lift(const void* a, lq_dtype a_dt, int64_t B, int64_t n, const
                        lq_dtype t_dt, const float* M, int d, int D, void* out, lq_dtype out_dt,
                        hipStream_t st);
 
-// The matrix-core lift (k_lift_mfma.hip) takes over from this many tokens
+// The matrix-core lift (k_lift_mfma.hip) takes over from 8 tokens (from 4
+// when n >= 12288, where T^-1 is large enough for its wider reads to pay)
 // when a and T^-1 share a 16-bit type and d divides 128 (d = 4, 8, 16, 32).
-constexpr int64_t kLiftMfmaMinTokens = 17;
 bool lift_mfma_applies(lq_dtype a_dt, lq_dtype t_dt, int64_t B, int64_t n, int d, int D);
 hipError_t launch_lift_mfma(const void* a, lq_dtype dt, int64_t B, int64_t n, const void* t_inv,
                             const float* M, int d, int D, void* out, lq_dtype out_dt,

@@ -77,10 +77,13 @@ LIFT_CASES = [  # (n, d, D, B, act dtype)
     (512, 8, 20, 16, "bf16"), (256, 16, 40, 33, "bf16"), (384, 8, 16, 4, "f16"),
     (384, 3, 7, 2, "bf16"), (256, 64, 128, 1, "f16"), (1280, 40, 100, 2, "bf16"),
     (640, 32, 80, 20, "f16"),
-    # 17 tokens and more with a and T^-1 of one 16-bit type and d | 128 take
-    # the matrix-core lift: ragged token tiles, D % 8 != 0, d = 4 .. 32
+    # 8 tokens and more (4 and more when n >= 12288) with a and T^-1 of one
+    # 16-bit type and d | 128 take the matrix-core lift: ragged token tiles,
+    # D % 8 != 0 (a_hat through LDS), d = 4 .. 32
     (1024, 8, 19, 130, "bf16"), (512, 4, 9, 17, "f16"), (384, 16, 40, 257, "f16"),
-    (2048, 8, 20, 64, "bf16"), (256, 32, 64, 40, "bf16"),
+    (2048, 8, 20, 64, "bf16"), (256, 32, 64, 40, "bf16"), (1024, 16, 40, 8, "f16"),
+    (2048, 4, 9, 9, "bf16"), (16384, 8, 19, 4, "bf16"), (12288, 32, 80, 5, "f16"),
+    (12160, 8, 19, 4, "bf16"),
 ]
 
 
