@@ -19,6 +19,8 @@
 //     codes, walked in Gray-code order so C_t moves by one column of M per
 //     step (exact every 64 steps).  A running minimum e_min with rescaling
 //     keeps every exponent <= 0; sums fold from 64-step chunks into totals.
+//     Within a chunk the code bits >= 6 do not change, so their sums of p
+//     are the chunk's sum of p: only the six low bits are summed per code.
 //     Writes (e_min, Z, sum p [bit j]) per slice and sample.
 //   fwd_merge: lane = sample; merges the slices, forms y_hat, r, g, g . y_hat
 //     and the loss, keeps (e_min, 1/Z, g . y_hat, g) per sample, and sums the
@@ -38,7 +40,8 @@ namespace lq {
 namespace {
 
 constexpr int kT = 256;
-constexpr uint32_t kResync = 64;
+constexpr int kLowBits = 6;
+constexpr uint32_t kResync = 1u << kLowBits;   // Gray-code steps between exact recomputations
 constexpr int kMaxBits = 24;
 
 using f32x4 = float __attribute__((ext_vector_type(4)));
@@ -89,9 +92,26 @@ __global__ void __launch_bounds__(kT) softmin_fwd_partial_kernel(
   };
   const float kInf = __builtin_inff();
   float emin = kInf, Z = 0.f, zl = 0.f;
-  float num[XM], numl[XM];
+  float num[XM], numl[kLowBits];
 #pragma unroll
-  for (int j = 0; j < XM; ++j) num[j] = numl[j] = 0.f;
+  for (int j = 0; j < XM; ++j) num[j] = 0.f;
+#pragma unroll
+  for (int j = 0; j < kLowBits; ++j) numl[j] = 0.f;
+  // Close a chunk whose codes share their bits >= kLowBits with tp: those
+  // bits' sums are the chunk's sum of p, the low bits' were kept per code.
+  auto fold = [&](uint32_t tp) {
+#pragma unroll
+    for (int j = 0; j < XM; ++j) {
+      if (j < kLowBits) {
+        num[j] += numl[j];
+        numl[j] = 0.f;
+      } else if (j < D && ((tp >> j) & 1u)) {
+        num[j] += zl;
+      }
+    }
+    Z += zl;
+    zl = 0.f;
+  };
   uint32_t t = blockIdx.y * slice_len;
   for (uint32_t i = 0; i < slice_len; ++i) {
     int k = 0;
@@ -100,13 +120,7 @@ __global__ void __launch_bounds__(kT) softmin_fwd_partial_kernel(
       t ^= 1u << k;
     }
     if (i % kResync == 0) {
-      Z += zl;
-      zl = 0.f;
-#pragma unroll
-      for (int j = 0; j < XM; ++j) {
-        num[j] += numl[j];
-        numl[j] = 0.f;
-      }
+      fold(t ^ (i ? 1u << k : 0u));                 // the last code of the chunk that ends here
       exact_c(t);
     } else {
       axpy_col<DM>(c, (t >> k) & 1u ? 2.f : -2.f, &mt[k][0]);
@@ -122,24 +136,23 @@ __global__ void __launch_bounds__(kT) softmin_fwd_partial_kernel(
       Z *= sc;
       zl *= sc;
 #pragma unroll
-      for (int j = 0; j < XM; ++j) {
-        num[j] *= sc;
-        numl[j] *= sc;
-      }
+      for (int j = 0; j < XM; ++j) num[j] *= sc;
+#pragma unroll
+      for (int j = 0; j < kLowBits; ++j) numl[j] *= sc;
       emin = e;
     }
     const float p = expf_fast(-T * (e - emin));
     zl += p;
 #pragma unroll
-    for (int j = 0; j < XM; ++j)
+    for (int j = 0; j < kLowBits; ++j)
       if (j < D) numl[j] = fmaf((t >> j) & 1u ? 1.f : 0.f, p, numl[j]);
   }
-  Z += zl;
+  fold(t);
   if (!act) return;
   float* o = part + (static_cast<int64_t>(blockIdx.y) * N + n) * (D + 2);
   o[0] = emin;
   o[1] = Z;
-  for (int j = 0; j < D; ++j) o[2 + j] = num[j] + numl[j];
+  for (int j = 0; j < D; ++j) o[2 + j] = num[j];
 }
 
 // Sum over the workgroup's 256 lanes of a[lane][r] * b[lane][j] (r < d,
