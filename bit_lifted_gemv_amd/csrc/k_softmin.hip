@@ -28,6 +28,8 @@
 //   bwd: lane = code t, workgroup = 256 codes x one slice of the samples
 //     (staged in LDS, read as broadcasts); accumulates beta_t and
 //     sum_n b_nt w_n, then sums 2T (sum b w - beta C_t) y_t^T over its codes.
+//     The code bits >= 8 are those of the workgroup, so g_n . y_t over them
+//     is formed once per staged sample; a pair adds only the 8 low bits.
 //   reduce: the forward and backward partial rows are added column-wise by
 //     a fixed tree (16 rows per node, consecutive rows, left to right),
 //     then one small kernel forms the loss and the gradient.
@@ -248,14 +250,19 @@ __global__ void __launch_bounds__(kT) softmin_bwd_kernel(
     const float* __restrict__ W, int N, const float* __restrict__ M, int d, int D, float T,
     int n_slice, const float* __restrict__ samp, float* __restrict__ bpart) {
   __shared__ __align__(16) float mt[XM][DM];
-  // one pool: the staged samples (sw, sg, se, srz, sgy) during the loop, the
-  // outer-sum rows (sa, sb) after it
-  __shared__ __align__(16) float pool[kT * (DM + XM + 3)];
+  // one pool: the staged samples (sw, sg, se, srz, sgy, sgh) during the loop,
+  // the outer-sum rows (sa, sb) after it
+  __shared__ __align__(16) float pool[kT * (DM + XM + 4)];
   float(*sw)[DM] = reinterpret_cast<float(*)[DM]>(pool);
   float(*sg)[XM] = reinterpret_cast<float(*)[XM]>(pool + kT * DM);
   float* se = pool + kT * (DM + XM);
   float* srz = se + kT;
   float* sgy = srz + kT;
+  // g_n . y_t over the code bits >= kLowJ, the same for the workgroup's 256
+  // codes (bits >= 8 of t are those of blockIdx.x)
+  float* sgh = sgy + kT;
+  constexpr int kLowJ = XM < 8 ? XM : 8;
+  const uint32_t tblk = blockIdx.x * kT;
   float(*sa)[DM + 1] = reinterpret_cast<float(*)[DM + 1]>(pool);
   float(*sb)[XM + 1] = reinterpret_cast<float(*)[XM + 1]>(pool + kT * (DM + 1));
   stage_m<DM, XM>(M, d, D, mt);
@@ -290,6 +297,11 @@ __global__ void __launch_bounds__(kT) softmin_bwd_kernel(
       se[threadIdx.x] = o[0];
       srz[threadIdx.x] = o[1];
       sgy[threadIdx.x] = o[2];
+      float hi = 0.f;
+#pragma unroll
+      for (int j = kLowJ; j < XM; ++j)
+        if (j < D) hi = fmaf((tblk >> j) & 1u ? 1.f : -1.f, o[3 + j], hi);
+      sgh[threadIdx.x] = hi;
     }
     __syncthreads();
     float bl = 0.f;
@@ -309,9 +321,9 @@ __global__ void __launch_bounds__(kT) softmin_bwd_kernel(
           e = fmaf(dr, dr, e);
         }
       }
-      float a = 0.f;
+      float a = sgh[u];
 #pragma unroll
-      for (int j4 = 0; j4 < XM / 4; ++j4) {
+      for (int j4 = 0; j4 < kLowJ / 4; ++j4) {
         const f32x4 g = *reinterpret_cast<const f32x4*>(&sg[u][4 * j4]);
 #pragma unroll
         for (int qq = 0; qq < 4; ++qq) a = fmaf(ys[4 * j4 + qq], g[qq], a);
