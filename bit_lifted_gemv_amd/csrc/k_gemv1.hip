@@ -262,8 +262,13 @@ __global__ void __launch_bounds__(kThreads, 1) gemv1_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t t_begin = sc.start[blockIdx.x];
-  const int64_t t_end = sc.start[blockIdx.x + 1];
+  // Workgroups are dispatched round-robin over the 8 XCDs.  With the lift in
+  // the prologue, the ones on an XCD take consecutive ranges, so that the
+  // workgroups sharing a slice (and its T^-1 rows) mostly share an L2.
+  int wg = blockIdx.x;
+  if (kFused && (sc.G & 7) == 0) wg = (blockIdx.x & 7) * (sc.G >> 3) + (blockIdx.x >> 3);
+  const int64_t t_begin = sc.start[wg];
+  const int64_t t_end = sc.start[wg + 1];
   if (t_begin >= t_end) return;
   const int sl_first = static_cast<int>(t_begin / sc.NG);
   const int sl_last = static_cast<int>((t_end - 1) / sc.NG);
