@@ -14,8 +14,11 @@
 // One wave per group.  Each lane walks a contiguous range of candidate
 // indices in Gray-code order, so consecutive candidates differ in one bit k:
 // the search moves B [w; v] by +-2 B[:, d + k] and the exhaustive walk moves
-// the residual w - M y by -+2 M[:, k], both recomputed exactly every 32 steps
-// to bound the drift of the running sums.  The wave then reduces the lanes'
+// the residual w - M y by -+2 M[:, k].  In the search such a step flips only
+// a few signs of B [w; v] (about 4 of 32 for the table's codes), so the
+// residual moves by -+2 M[:, j] for each flipped sign j instead of being
+// formed anew (D d multiply-adds).  All running sums are recomputed exactly
+// every 32 steps to bound their drift.  The wave then reduces the lanes'
 // best (error, index) pairs.
 #include "lq_internal.h"
 
@@ -187,6 +190,7 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(
   float best_e = __builtin_inff();
   uint32_t best_t = 0xffffffffu;
   uint32_t best_m = 0;
+  uint32_t mprev = 0;                              // mask that res belongs to (search)
   uint32_t t = t0;
   for (uint32_t i = 0; i < R; ++i) {
     int k = 0;
@@ -212,7 +216,23 @@ __global__ void __launch_bounds__(kThreads) encode_kernel(
 #pragma unroll
       for (int j = 0; j < XM; ++j)
         if (j < D) m |= (x[j] >= 0.f ? 1u : 0u) << j;
-      exact_res(m);
+      if (resync) {
+        exact_res(m);
+      } else {
+        // one step of v moves x along one column of B, which flips only a
+        // few signs (about 4 of 32): update the residual column by column
+        for (uint32_t diff = m ^ mprev; diff; diff &= diff - 1) {
+          const int j = __builtin_ctz(diff);
+          const float sj = (m >> j) & 1u ? -2.f : 2.f;
+#pragma unroll
+          for (int r4 = 0; r4 < DM / 4; ++r4) {
+            const f32x4 c = *reinterpret_cast<const f32x4*>(&mt[j][4 * r4]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) res[4 * r4 + q] = fmaf(sj, c[q], res[4 * r4 + q]);
+          }
+        }
+      }
+      mprev = m;
     } else {
       m = t;
       if (resync) {
