@@ -424,6 +424,305 @@ hipError_t launch_cols(const float* zt, int64_t B, int n1, int n2, const float* 
   }
 }
 
+// ---- one launch for many tokens (small enough factors).  A workgroup of 8
+// waves stages P2^-1, P1^-1, M and 1/s2 in LDS once, then takes tokens b =
+// blockIdx.x, blockIdx.x + gridDim.x, ...: X = a_b / s1 into LDS, Z = X
+// P2^-T and then Y = P1^-1 Z as 16 x 16 float32 MFMA tiles with both operands
+// read from LDS (two tiles per wave at a time, so that two accumulation
+// chains interleave), and the per-group M^T step as a third MFMA product
+// whose result lanes hold four consecutive outputs of one group.  No Zt
+// round trip through memory.  Row strides: n2 + 4 floats for X, Y and
+// P2^-1 and n1 + 4 for P1^-1 (the 16 rows x 4 k of an operand read land in
+// distinct banks), n2 + 16 for Z (read as 4 rows x 16 columns).
+// Eight consecutive activations as float (i % 8 == 0, 16-byte aligned).
+template <int DT>
+__device__ __forceinline__ void load8_as_float(const void* base, int64_t i, float (&v)[8]) {
+  if constexpr (DT == LQ_F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + i);
+    const float4 x = p[0], y = p[1];
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+  } else {
+    const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + i);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = half_to_float<DT>(w[e] & 0xFFFFu);
+      v[2 * e + 1] = half_to_float<DT>(w[e] >> 16);
+    }
+  }
+}
+
+// Four consecutive outputs (i % 4 == 0, aligned) as one vector store.
+template <int O_DT>
+__device__ __forceinline__ void store4_out(void* out, int64_t i, const float* v) {
+  if constexpr (O_DT == LQ_F32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + i) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    uint16_t h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      h[e] = O_DT == LQ_F16 ? float_to_f16_bits_rne(v[e]) : float_to_bf16_bits_rne(v[e]);
+    uint2 q;
+    q.x = h[0] | (static_cast<uint32_t>(h[1]) << 16);
+    q.y = h[2] | (static_cast<uint32_t>(h[3]) << 16);
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + i) = q;
+  }
+}
+
+constexpr int kFWaves = 8;
+constexpr int kFThreads = 64 * kFWaves;
+constexpr int kFJT = 4;                    // D <= 64: at most 4 16-wide output tiles
+constexpr int kFKS = 8;                    // d <= 32: at most 8 4-deep k steps
+
+__host__ __device__ constexpr size_t fused_lds_floats(int n1, int n2, int d, int D) {
+  return static_cast<size_t>(n1) * (n2 + 4) + static_cast<size_t>(n1) * (n2 + 16) +
+         static_cast<size_t>(n2) * (n2 + 4) + static_cast<size_t>(n1) * (n1 + 4) +
+         static_cast<size_t>(d) * D + static_cast<size_t>(n1) * n2 / d;
+}
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// JT = ceil(D / 16) output tiles and KS >= ceil(d / 4) k steps of the
+// per-group product, fixed at compile time so that its MFMAs run without
+// branches between them (operands past d or D are zero).
+template <int JT, int KS>
+__global__ void __launch_bounds__(kFThreads, 1) kron_fused_kernel(
+    const void* __restrict__ a, const float* __restrict__ s1, const float* __restrict__ p1,
+    const float* __restrict__ p2, const float* __restrict__ s2, const float* __restrict__ M,
+    void* __restrict__ out, int B, int n1, int n2, int d, int D, int a_dt, int out_dt) {
+  extern __shared__ float lds[];
+  const int n = n1 * n2;
+  const int ldx = n2 + 4, ldz = n2 + 16, ldp2 = n2 + 4, ldp1 = n1 + 4;
+  float* sX = lds;                          // [n1][ldx]: X, then Y
+  float* sZ = sX + n1 * ldx;                // [n1][ldz]
+  float* sP2 = sZ + n1 * ldz;               // [n2][ldp2]
+  float* sP1 = sP2 + n2 * ldp2;             // [n1][ldp1]
+  float* sM = sP1 + n1 * ldp1;              // [d][D]
+  float* sR2 = sM + d * D;                  // [n / d]: 1 / s2
+  const int tid = threadIdx.x;
+  for (int i = tid; i < n2 * n2; i += kFThreads) sP2[(i / n2) * ldp2 + i % n2] = p2[i];
+  for (int i = tid; i < n1 * n1; i += kFThreads) sP1[(i / n1) * ldp1 + i % n1] = p1[i];
+  for (int i = tid; i < d * D; i += kFThreads) sM[i] = M[i];
+  for (int i = tid; i < n / d; i += kFThreads) sR2[i] = 1.f / s2[i];
+
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15;
+  const int kq = lane >> 4;
+  const int tj_n = n2 / 16;
+  const int tiles = (n1 / 16) * tj_n;
+  const int64_t K = static_cast<int64_t>(n / d) * D;
+  for (int b = blockIdx.x; b < B; b += gridDim.x) {
+    __syncthreads();                        // staging done / the previous token's Y read
+    // eight consecutive values per thread and pass (n2 % 8 == 0: a run stays
+    // in one row of X)
+    for (int c = 8 * tid; c < n; c += 8 * kFThreads) {
+      float v[8];
+      const int64_t ai = static_cast<int64_t>(b) * n + c;
+      if (a_dt == LQ_F32)
+        load8_as_float<LQ_F32>(a, ai, v);
+      else if (a_dt == LQ_F16)
+        load8_as_float<LQ_F16>(a, ai, v);
+      else
+        load8_as_float<LQ_BF16>(a, ai, v);
+      const float4 r0 = *reinterpret_cast<const float4*>(s1 + c);
+      const float4 r1 = *reinterpret_cast<const float4*>(s1 + c + 4);
+      const float sv[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+      float* xr = sX + (c / n2) * ldx + c % n2;
+      float4 o0, o1;
+      o0.x = v[0] / sv[0]; o0.y = v[1] / sv[1]; o0.z = v[2] / sv[2]; o0.w = v[3] / sv[3];
+      o1.x = v[4] / sv[4]; o1.y = v[5] / sv[5]; o1.z = v[6] / sv[6]; o1.w = v[7] / sv[7];
+      reinterpret_cast<float4*>(xr)[0] = o0;
+      reinterpret_cast<float4*>(xr)[1] = o1;
+    }
+    __syncthreads();
+    // Z = X P2^-T: A[i][k] = X[i][k], B[k][j] = P2^-1[j][k]; the result lane
+    // holds column l16 and rows 4 kq + e of its tile
+#pragma unroll 1
+    for (int t0 = 2 * wave; t0 < tiles; t0 += 2 * kFWaves) {
+      const int t1 = t0 + 1 < tiles ? t0 + 1 : t0;
+      const float* xa0 = sX + ((t0 / tj_n) * 16 + l16) * ldx + kq;
+      const float* xa1 = sX + ((t1 / tj_n) * 16 + l16) * ldx + kq;
+      const float* pb0 = sP2 + ((t0 % tj_n) * 16 + l16) * ldp2 + kq;
+      const float* pb1 = sP2 + ((t1 % tj_n) * 16 + l16) * ldp2 + kq;
+      f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0;
+#pragma unroll 1
+      for (int k = 0; k < n2; k += 16) {        // n2 % 16 == 0: operands of 4 steps first
+        float a0[4], b0[4], a1[4], b1[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          a0[u] = xa0[k + 4 * u];
+          b0[u] = pb0[k + 4 * u];
+          a1[u] = xa1[k + 4 * u];
+          b1[u] = pb1[k + 4 * u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          c0 = mfma4(a0[u], b0[u], c0);
+          c1 = mfma4(a1[u], b1[u], c1);
+        }
+      }
+      float* z0 = sZ + ((t0 / tj_n) * 16 + 4 * kq) * ldz + (t0 % tj_n) * 16 + l16;
+      float* z1 = sZ + ((t1 / tj_n) * 16 + 4 * kq) * ldz + (t1 % tj_n) * 16 + l16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        z0[e * ldz] = c0[e];
+        z1[e * ldz] = c1[e];
+      }
+    }
+    __syncthreads();
+    // Y = P1^-1 Z into sX: A[i][k] = P1^-1[i][k], B[k][j] = Z[k][j]
+#pragma unroll 1
+    for (int t0 = 2 * wave; t0 < tiles; t0 += 2 * kFWaves) {
+      const int t1 = t0 + 1 < tiles ? t0 + 1 : t0;
+      const float* pa0 = sP1 + ((t0 / tj_n) * 16 + l16) * ldp1 + kq;
+      const float* pa1 = sP1 + ((t1 / tj_n) * 16 + l16) * ldp1 + kq;
+      const float* zb0 = sZ + kq * ldz + (t0 % tj_n) * 16 + l16;
+      const float* zb1 = sZ + kq * ldz + (t1 % tj_n) * 16 + l16;
+      f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0;
+#pragma unroll 1
+      for (int k = 0; k < n1; k += 16) {        // n1 % 16 == 0
+        float a0[4], b0[4], a1[4], b1[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          a0[u] = pa0[k + 4 * u];
+          b0[u] = zb0[(k + 4 * u) * ldz];
+          a1[u] = pa1[k + 4 * u];
+          b1[u] = zb1[(k + 4 * u) * ldz];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          c0 = mfma4(a0[u], b0[u], c0);
+          c1 = mfma4(a1[u], b1[u], c1);
+        }
+      }
+      float* y0 = sX + ((t0 / tj_n) * 16 + 4 * kq) * ldx + (t0 % tj_n) * 16 + l16;
+      float* y1 = sX + ((t1 / tj_n) * 16 + 4 * kq) * ldx + (t1 % tj_n) * 16 + l16;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y0[e * ldx] = c0[e];
+        y1[e * ldx] = c1[e];
+      }
+    }
+    __syncthreads();
+    // a_hat[b][g D + jj] = (1 / s2[g]) sum_r M[r][jj] Y[channel g d + r] as a
+    // third product, C = M^T U^T (D x groups): A[i][k] = M[k][jt 16 + i],
+    // B[k][j] = Y of group gt 16 + j at r = k (a group lies in one row of Y,
+    // n2 % d == 0).  A wave takes whole tiles of 16 groups: its results go to
+    // its own part of the (now free) Z buffer as [group][jj], then the wave
+    // writes the tile's 16 D consecutive outputs in 4-value pieces.
+    const int gtiles = n / d / 16;
+    float* stage = sZ + wave * (16 * D);
+    // the A operand (M) is the same for every group tile: load it once
+    float av[JT][KS];
+#pragma unroll
+    for (int jt = 0; jt < JT; ++jt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int r = 4 * ks + kq;
+        const int jm = jt * 16 + l16;
+        // clamped address, then zeroed: no per-lane branch around the load
+        const float v = sM[min(r, d - 1) * D + min(jm, D - 1)];
+        av[jt][ks] = (r < d && jm < D) ? v : 0.f;
+      }
+#pragma unroll 1
+    for (int gt = wave; gt < gtiles; gt += kFWaves) {
+      const int g = gt * 16 + l16;                        // this lane's B column / group
+      const int c0 = g * d;
+      const float* yr = sX + (c0 / n2) * ldx + c0 % n2;
+      float bv[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int r = 4 * ks + kq;
+        const float v = yr[min(r, d - 1)];
+        bv[ks] = r < d ? v : 0.f;
+      }
+      const float sc = sR2[g];
+      f32x4 c[JT];
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt) c[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int jt = 0; jt < JT; ++jt) c[jt] = mfma4(av[jt][ks], bv[ks], c[jt]);
+#pragma unroll
+      for (int jt = 0; jt < JT; ++jt) {
+        const int jj0 = jt * 16 + 4 * kq;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (jj0 + e < D) stage[l16 * D + jj0 + e] = c[jt][e] * sc;
+      }
+      // the wave's own LDS writes are seen by its later reads in order
+      const int64_t o = static_cast<int64_t>(b) * K + static_cast<int64_t>(gt) * 16 * D;
+      for (int q = lane; q < 4 * D; q += 64) {
+        if (out_dt == LQ_F32)
+          store4_out<LQ_F32>(out, o + 4 * q, stage + 4 * q);
+        else if (out_dt == LQ_F16)
+          store4_out<LQ_F16>(out, o + 4 * q, stage + 4 * q);
+        else
+          store4_out<LQ_BF16>(out, o + 4 * q, stage + 4 * q);
+      }
+    }
+  }
+}
+
+bool fused_applies(int64_t B, int n1, int n2, int d, int D, const void* a, const float* s1,
+                   const void* out) {
+  const bool aligned = reinterpret_cast<uintptr_t>(a) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(s1) % 16 == 0 &&
+                       reinterpret_cast<uintptr_t>(out) % 16 == 0;
+  return aligned && B >= 64 && d <= 4 * kFKS && D <= 16 * kFJT && n1 % 16 == 0 &&
+         n2 % 16 == 0 && n2 % d == 0 &&
+         (n1 * n2 / d) % 16 == 0 && 16 * D <= n1 * (n2 + 16) / kFWaves &&
+         fused_lds_floats(n1, n2, d, D) * sizeof(float) <= 160 * 1024;
+}
+
+template <int JT, int KS>
+hipError_t launch_fused_jk(const void* a, lq_dtype a_dt, int64_t B, int n1, int n2,
+                           const float* s1, const float* p1, const float* p2, const float* s2,
+                           const float* M, int d, int D, void* out, lq_dtype out_dt,
+                           hipStream_t st) {
+  const size_t lds = fused_lds_floats(n1, n2, d, D) * sizeof(float);
+  if (lds > 65536) {
+    const hipError_t e = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(kron_fused_kernel<JT, KS>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
+  }
+  int cus = num_cus();
+  const int grid = static_cast<int>(B < cus ? B : cus);
+  hipLaunchKernelGGL((kron_fused_kernel<JT, KS>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kFThreads), lds, st, a, s1, p1, p2, s2, M, out, static_cast<int>(B),
+                     n1, n2, d, D, static_cast<int>(a_dt), static_cast<int>(out_dt));
+  return hipGetLastError();
+}
+
+template <int JT>
+hipError_t launch_fused_j(const void* a, lq_dtype a_dt, int64_t B, int n1, int n2,
+                          const float* s1, const float* p1, const float* p2, const float* s2,
+                          const float* M, int d, int D, void* out, lq_dtype out_dt,
+                          hipStream_t st) {
+  if (d <= 4) return launch_fused_jk<JT, 1>(a, a_dt, B, n1, n2, s1, p1, p2, s2, M, d, D, out, out_dt, st);
+  if (d <= 8) return launch_fused_jk<JT, 2>(a, a_dt, B, n1, n2, s1, p1, p2, s2, M, d, D, out, out_dt, st);
+  if (d <= 16) return launch_fused_jk<JT, 4>(a, a_dt, B, n1, n2, s1, p1, p2, s2, M, d, D, out, out_dt, st);
+  return launch_fused_jk<JT, 8>(a, a_dt, B, n1, n2, s1, p1, p2, s2, M, d, D, out, out_dt, st);
+}
+
+hipError_t launch_fused(const void* a, lq_dtype a_dt, int64_t B, int n1, int n2,
+                        const float* s1, const float* p1, const float* p2, const float* s2,
+                        const float* M, int d, int D, void* out, lq_dtype out_dt,
+                        hipStream_t st) {
+  switch ((D + 15) / 16) {
+    case 1: return launch_fused_j<1>(a, a_dt, B, n1, n2, s1, p1, p2, s2, M, d, D, out, out_dt, st);
+    case 2: return launch_fused_j<2>(a, a_dt, B, n1, n2, s1, p1, p2, s2, M, d, D, out, out_dt, st);
+    case 3: return launch_fused_j<3>(a, a_dt, B, n1, n2, s1, p1, p2, s2, M, d, D, out, out_dt, st);
+    default: return launch_fused_j<4>(a, a_dt, B, n1, n2, s1, p1, p2, s2, M, d, D, out, out_dt, st);
+  }
+}
+
 }  // namespace
 
 bool lift_kron_shape_ok(int64_t n, int n1, int d, int D) {
@@ -443,6 +742,11 @@ hipError_t launch_lift_kron(const void* a, lq_dtype a_dt, int64_t B, int64_t n, 
                             const float* s2, const float* M, int d, int D, void* out,
                             lq_dtype out_dt, void* ws, hipStream_t st) {
   const int n2 = static_cast<int>(n / n1);
+#ifndef LQ_KRON_FUSED
+#define LQ_KRON_FUSED 1
+#endif
+  if (LQ_KRON_FUSED && fused_applies(B, n1, n2, d, D, a, s1, out))
+    return launch_fused(a, a_dt, B, n1, n2, s1, p1_inv, p2_inv, s2, M, d, D, out, out_dt, st);
   float* zt = static_cast<float*>(ws);
   hipError_t e;
   switch (a_dt) {

@@ -117,6 +117,9 @@ KRON_CASES = [  # (n, n1, d, D, B, act dtype): n2 = n / n1 <= 128, n2 % d == 0
     (384, 3, 4, 9, 2, "bf16"), (960, 12, 8, 16, 7, "bf16"), (6, 2, 3, 5, 1, "f32"),
     # large batches: several column blocks per wave, a ragged last column slab
     (8192, 64, 16, 40, 512, "bf16"), (2048, 16, 8, 19, 300, "f16"),
+    # 64 tokens and more with small factors take the single-launch kernel:
+    # D % 4 != 0, float32 activations, several tokens per workgroup
+    (4096, 32, 8, 19, 70, "bf16"), (2048, 16, 4, 9, 65, "f16"), (1024, 16, 8, 20, 300, "f32"),
 ]
 
 
@@ -141,8 +144,9 @@ def test_lift_kron_float32(dev, n, n1, d, D, B, dt):
 
 
 @pytest.mark.parametrize("odt", [torch.float16, torch.bfloat16])
-def test_lift_kron_16bit_outputs(dev, odt):
-    n, n1, d, D, B = 8192, 64, 16, 40, 9
+@pytest.mark.parametrize("B", [9, 96])   # two launches / the single-launch kernel
+def test_lift_kron_16bit_outputs(dev, odt, B):
+    n, n1, d, D = 8192, 64, 16, 40
     f, M, a = _kron_inputs(n, n1, d, D, B, "bf16", 77)
     ref = O.lift_kron(a, f.s1, f.p1_inv, f.p2_inv, f.s2, M, d, D, "bf16")
     t = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)
