@@ -9,6 +9,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -39,24 +40,31 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False, out: str = LIB) -> str:
-    """Compile every csrc/*.hip into one shared library; returns its path."""
+def _compile(src: str, objdir: str, verbose: bool) -> str:
+    obj = os.path.join(objdir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = "\n".join(ln for ln in (r.stdout + r.stderr).splitlines()
+                     if "packed-fp32-ops" not in ln)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{msgs}")
+    if verbose and msgs.strip():
+        print(msgs, flush=True)
+    return obj
+
+
+def build(verbose: bool = False, out: str = LIB, jobs: int = 0) -> str:
+    """Compile every csrc/*.hip into one shared library; returns its path.
+    The translation units compile in parallel (jobs = 0: one per CPU, at
+    most 16)."""
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
-    for src in sources():
-        obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        msgs = "\n".join(ln for ln in (r.stdout + r.stderr).splitlines()
-                         if "packed-fp32-ops" not in ln)
-        if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {src}:\n{msgs}")
-        if verbose and msgs.strip():
-            print(msgs, flush=True)
-        objs.append(obj)
+    srcs = sources()
+    jobs = jobs or min(16, os.cpu_count() or 1, len(srcs))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, objdir, verbose), srcs))
     tmp = out + ".tmp"
     # rocBLAS carries the plain float16 GEMM of the decode-weights product
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,

@@ -368,3 +368,84 @@ def test_kron_group_scale_folds_into_M():
     u1 = O.transform_kron(a, s1, p1, p2, np.ones(n // d), d)
     folded = np.concatenate([(u1[:, g * d:(g + 1) * d] @ M) / s2g[g] for g in range(n // d)], axis=1)
     np.testing.assert_allclose(ah, folded, rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------- Kronecker lift and layer glue
+def _kron_lift_case():
+    ln = _lines("kron_lift_worked.txt")[0]
+    f = [np.array([float(x) for x in part.split()]) for part in ln.split(";")]
+    a, s1, p1, p2, s2g, M, ahat, words, s, o = f
+    return dict(a=a.astype(np.float32)[None], s1=s1.astype(np.float32),
+                p1=p1.reshape(2, 2).astype(np.float32), p2=p2.reshape(2, 2).astype(np.float32),
+                s2g=s2g.astype(np.float32), M=M.reshape(2, 3).astype(np.float32), d=2, D=3,
+                ahat=ahat, packed=words.astype(np.uint32)[:, None], s=s.astype(np.float32), o=o)
+
+
+def test_lift_kron_worked_example():
+    """lift_kron on the hand-worked case (tests/golden/kron_lift_worked.txt)."""
+    c = _kron_lift_case()
+    got = O.lift_kron(c["a"], c["s1"], c["p1"], c["p2"], c["s2g"], c["M"], c["d"], c["D"], "f32")
+    np.testing.assert_array_equal(got[0], c["ahat"])
+
+
+def test_forward_kron_worked_example():
+    """forward_kron (unpack, W_hat = M y, Kronecker T^-1, dense product, s) on
+    the hand-worked case."""
+    c = _kron_lift_case()
+    got = O.forward_kron(c["packed"], 6, c["M"], c["s1"], c["p1"], c["p2"], c["s2g"], c["s"],
+                         c["a"], c["d"], c["D"], "f32")
+    np.testing.assert_array_equal(got[0], c["o"])
+
+
+@pytest.mark.parametrize("slip", ["s2 dropped", "P2 transposed", "P1 transposed", "s1 dropped",
+                                  "a_hat scaled by s"])
+def test_kron_worked_example_catches_planted_slips(slip):
+    """Each plausible slip in the Kronecker glue changes the hand-worked result."""
+    c = _kron_lift_case()
+    args = dict(s1=c["s1"], p1=c["p1"], p2=c["p2"], s2g=c["s2g"])
+    if slip == "s2 dropped":
+        args["s2g"] = np.ones_like(c["s2g"])
+    elif slip == "P2 transposed":
+        args["p2"] = np.ascontiguousarray(c["p2"].T)
+    elif slip == "P1 transposed":
+        args["p1"] = np.ascontiguousarray(c["p1"].T)
+    elif slip == "s1 dropped":
+        args["s1"] = np.ones_like(c["s1"])
+    got = O.lift_kron(c["a"], args["s1"], args["p1"], args["p2"], args["s2g"], c["M"], c["d"],
+                      c["D"], "f32")[0]
+    if slip == "a_hat scaled by s":
+        got = got * c["s"][0]
+    assert not np.array_equal(got, c["ahat"])
+
+
+@pytest.mark.parametrize("n1,n2,d,D,dtype", [(4, 16, 8, 19, "bf16"), (3, 40, 10, 24, "f16"),
+                                              (2, 32, 4, 9, "f32")])
+def test_forward_kron_identity_factor_equals_block_diagonal_forward(n1, n2, d, D, dtype):
+    """P1 = I, s1 = 1, s2 = 1: the Kronecker layer is the block-diagonal layer
+    with T^-1 = blockdiag(P2^-1) (the separately pinned `forward`), through
+    every step of the glue (decode, unpack, reconstruct, transform, s)."""
+    rng = np.random.default_rng(n1 * 1000 + n2 * 10 + d)
+    n, m, B = n1 * n2, 7, 3
+    K = n // d * D
+    p2 = rng.standard_normal((n2, n2)).astype(np.float32)
+    M = rng.standard_normal((d, D)).astype(np.float32)
+    s = rng.uniform(0.5, 2, m).astype(np.float32)
+    a = synth.to_storage(rng.standard_normal((B, n)).astype(np.float32), dtype)
+    signs = rng.choice([-1, 1], size=(m, K)).astype(np.int8)
+    packed = O.pack_signs_ref(signs)
+    got = O.forward_kron(packed, K, M, np.ones(n, np.float32), np.eye(n1, dtype=np.float32), p2,
+                         np.ones(n // d, np.float32), s, a, d, D, dtype)
+    # the block-diagonal reconstruct route of `forward`, with the float32
+    # blocks P2^-1 converted exactly (forward itself decodes T^-1 in the
+    # activation's 16-bit type)
+    M64, s64, a64 = O.decode(M, "f32"), O.decode(s, "f32"), O.decode(a, dtype)
+    u = O.transform(a64, np.repeat(p2.astype(np.float64)[None], n1, axis=0))
+    w = O.reconstruct_weights(O.signs_from_packed(packed, K), M64, d, D)
+    ref = (w @ u.T).T * s64[None, :]
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    # and through the lifted route of the Kronecker lift
+    lifted = O.lifted_product(packed, K, O.lift_kron(a, np.ones(n, np.float32),
+                                                     np.eye(n1, dtype=np.float32), p2,
+                                                     np.ones(n // d, np.float32), M, d, D, dtype),
+                              s)
+    np.testing.assert_allclose(lifted, ref, rtol=1e-12, atol=1e-12)
