@@ -1,0 +1,465 @@
+// Product of 1-bit weights with float lifted activations for a few tokens on
+// the matrix cores:
+//   out[b][i] = s[i] * sum_k sigma_ik * a_hat[b][k],  sigma = 2*bit - 1
+// (LiftQuant notes, 关键设计 4: after the activation transform the layer is a
+// product of 1-bit weights with floats, scaled per row by s).
+//
+// Operands of v_mfma_scale_f32_16x16x128_f8f6f4.  A (16 rows x 128 lifted
+// positions) holds the signs as float4 (E2M1) values +-1: from a word of 32
+// sign bits, dword q of the lane's operand takes bits q, q + 4, ..., q + 28
+// (nibble t <- bit 4 t + q), so each dword is one shift and one bit-field
+// insert; a set bit gives -1 (the products carry -sigma and the partial sums
+// are negated back).  B (128 positions x 16 columns) holds the activations of
+// up to five tokens as three float8 (E4M3) parts each, in columns 3 b + p:
+// for each 1024-position slice and token, x is scaled by 2^e (e puts the
+// slice's largest |x| in [128, 256)), then p0 = fp8(x 2^e), p1 = fp8(16 r0),
+// p2 = fp8(16 r1) with r the remainders (exact in float32); the hardware
+// scale of column (b, p) is 2^(-e - 4 p), so the three columns of a token add
+// up to x with a relative error of about 2^-12 of the slice's largest
+// |x| at worst.  Products are exact and accumulate in float32.
+//
+// Position order.  Each 1024-position slice of a row is 128 bytes; lane
+// (r, G) of a 16-row tile loads bytes 16 G .. 16 G + 15 and 64 + 16 G ..
+// 64 + 16 G + 15 of row r (words 4 G + u and 16 + 4 G + u, u < 4).  MFMA
+// step u < 4 takes word 4 G + u from lane group G, step 4 + u word
+// 16 + 4 G + u.  Within a word, bit 4 t + q sits at A slot 8 q + t, which in
+// the float8 B operand is lane group (32 G + 8 q + t) % 64 / 16, byte
+// (8 q + t) % 16 + 16 G / 2 (the float8 operand holds positions 16 g ..
+// 16 g + 15 and 64 + 16 g .. 64 + 16 g + 15 of the step); the activation
+// parts are stored in that order.
+//
+// Work split (as the one-token table kernel): granule = 16 rows x one slice;
+// granules ordered (slice, row) and cut into one range per workgroup (one
+// workgroup of 8 waves per CU); each wave streams a contiguous run of
+// granules per slice with a ring of DEPTH granules of loads in flight.  At
+// the start of a slice the workgroup turns the slice's activations into the
+// float8 parts (in LDS), and each wave keeps the B operands of the slice's 8
+// steps in registers while it streams the slice's granules.  Each granule
+// leaves the 16 rows' sums of one slice per token in the workspace; a second
+// kernel adds each row's S partial sums in slice order, scales by s and
+// writes the row.  Deterministic.
+#include <type_traits>
+
+#include "lq_internal.h"
+
+namespace lq {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kSliceBits = 1024;
+constexpr int kSliceBytes = kSliceBits / 8;     // 128 bytes of a row per slice
+constexpr int kSteps = kSliceBits / 128;        // 8 MFMA steps per slice
+constexpr uint32_t kNoLoad = 0x80000000u;       // past every buffer range: loads give 0
+constexpr int kWaves = 8;                       // two waves per SIMD: 256 registers each
+constexpr int kDepth = 4;                       // granules of weights in flight per wave
+constexpr int kEarly = 2;                       // of them issued before the parts exist
+constexpr int kThreads = 64 * kWaves;
+constexpr int kGranuleRows = 16;
+constexpr int kMaxGroups = 256;
+constexpr double kStraddleCost = 0.1;           // a second slice: parts and padded runs
+
+struct Sched {
+  int64_t NG;   // 16-row granules per slice
+  int64_t T;    // granules in all: S * NG
+  int S;        // slices
+  int G;        // workgroups
+  int64_t start[kMaxGroups + 1];
+};
+
+// A operand from one word of 32 signs: dword q, nibble t <- bit 4 t + q;
+// bit 1 -> 0xA (-1.0), bit 0 -> 0x2 (+1.0).
+__device__ __forceinline__ i32x8 expand(uint32_t w) {
+  i32x8 a;
+  a[0] = static_cast<int>(((w << 3) & 0x88888888u) | 0x22222222u);
+  a[1] = static_cast<int>(((w << 2) & 0x88888888u) | 0x22222222u);
+  a[2] = static_cast<int>(((w << 1) & 0x88888888u) | 0x22222222u);
+  a[3] = static_cast<int>((w & 0x88888888u) | 0x22222222u);
+  a[4] = a[5] = a[6] = a[7] = 0;               // unused with a float4 A operand
+  return a;
+}
+
+__device__ __forceinline__ f32x4 mfma(const i32x8& a, const i32x8& b, const f32x4& c, int sc) {
+  // A: E2M1 (cbsz 4), scale 2^0; B: E4M3 (blgp 0), scale 2^(sc - 127)
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, 127, 0, sc);
+}
+
+// Byte offset, within a slice's parts, of position k (< 1024) for column
+// 0 and lane-group byte (the column adds 128 bytes each): step-major
+// [step][column][lane group][32 bytes].
+__device__ __forceinline__ int part_offset(int k, int ncol) {
+  const int w = k >> 5, bit = k & 31;
+  const int u = w < 16 ? (w & 3) : 4 + ((w - 16) & 3);
+  const int G = w < 16 ? (w >> 2) : ((w - 16) >> 2);
+  const int slot = 8 * (bit & 3) + (bit >> 2);
+  const int kap = 32 * G + slot;
+  const int g = (kap & 63) >> 4;
+  const int beta = (kap & 15) + (kap >= 64 ? 16 : 0);
+  return (u * ncol * 4 + g) * 32 + beta;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_from(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// NB: tokens (1..5); DEPTH: granules of weights in flight per wave.
+template <int NB, int DEPTH, bool SPLIT>
+__global__ void __launch_bounds__(kThreads, 1) gemv_f4_kernel(
+    const uint32_t* __restrict__ w, int64_t m, int64_t K, int64_t ldw,
+    const float* __restrict__ s, const float* __restrict__ ah, float* __restrict__ out,
+    float* __restrict__ partials, Sched sc, uint32_t w_bytes, uint32_t a_bytes) {
+  constexpr int NCOL = 3 * NB;
+  constexpr int kPartBytes = kSteps * NCOL * 4 * 32;          // per slice
+  __shared__ __attribute__((aligned(16))) uint8_t parts[2][kPartBytes];
+  __shared__ float mx[2][kWaves][NB];
+  __shared__ int esc[2][NB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t t_begin = sc.start[blockIdx.x];
+  const int64_t t_end = sc.start[blockIdx.x + 1];
+  if (t_begin >= t_end) return;
+  const int sl_first = static_cast<int>(t_begin / sc.NG);
+  const int sl_last = static_cast<int>((t_end - 1) / sc.NG);
+
+  const int r = lane & 15;           // A: row; B and D: column
+  const int G = lane >> 4;           // lane group
+  const int col = r;
+  const int cb = col < NCOL ? col / 3 : 0;                 // token of the column
+  const int cp = col < NCOL ? col - 3 * (col / 3) : 0;     // part of the column
+  const int col_c = col < NCOL ? col : 0;                  // column read (unused ones: any)
+
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(w), (short)0, static_cast<int>(w_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ares = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(ah), (short)0, static_cast<int>(a_bytes), 0x00020000);
+  const uint32_t row_bytes = static_cast<uint32_t>(ldw * 4);
+  const uint32_t granule_bytes = kGranuleRows * row_bytes;
+  const uint32_t lane_off0 = static_cast<uint32_t>(r) * row_bytes + 16 * G;
+  const uint32_t lane_off1 = lane_off0 + 64;
+
+  auto lo_of = [&](int sl) -> int {
+    const int64_t v = t_begin - (int64_t)sl * sc.NG;
+    return v > 0 ? static_cast<int>(v) : 0;
+  };
+  auto hi_of = [&](int sl) -> int {
+    const int64_t v = t_end - (int64_t)sl * sc.NG;
+    return static_cast<int>(v < sc.NG ? v : sc.NG);
+  };
+  auto run_a = [&](int sl) -> int {
+    const int lo = lo_of(sl);
+    return lo + (wave * (hi_of(sl) - lo)) / kWaves;
+  };
+  auto run_b = [&](int sl) -> int {
+    const int lo = lo_of(sl);
+    return lo + ((wave + 1) * (hi_of(sl) - lo)) / kWaves;
+  };
+
+  // Load cursor (scalar): each slice's run is processed in rounds of DEPTH
+  // ring slots, the last round padded with empty slots.
+  int ld_sl = sl_first - 1, ld_k = 0, ld_n = 0, ld_slots = 0;
+  uint32_t ld_off = 0;
+  auto ld_next_slice = [&]() {
+    do {
+      ++ld_sl;
+      ld_k = 0;
+      if (ld_sl <= sl_last) {
+        const int a = run_a(ld_sl);
+        ld_n = run_b(ld_sl) - a;
+        ld_slots = (ld_n + DEPTH - 1) / DEPTH * DEPTH;
+        ld_off = static_cast<uint32_t>(a) * granule_bytes +
+                 static_cast<uint32_t>(ld_sl) * kSliceBytes;
+      } else {
+        ld_n = 0;
+        ld_slots = 1 << 30;
+      }
+    } while (ld_slots == 0);
+  };
+  uint4 wb[DEPTH][2];
+  auto issue = [&](uint4 (&dst)[2]) {
+    const uint32_t so = ld_k < ld_n ? ld_off : kNoLoad;
+    const auto v0 = __builtin_amdgcn_raw_buffer_load_b128(wres, lane_off0, so, 0);
+    const auto v1 = __builtin_amdgcn_raw_buffer_load_b128(wres, lane_off1, so, 0);
+    ld_off += granule_bytes;
+    ++ld_k;
+    __builtin_memcpy(&dst[0], &v0, 16);
+    __builtin_memcpy(&dst[1], &v1, 16);
+  };
+
+  // Activation parts of slices sp and sp + 1 (the second if the range
+  // reaches it) into LDS slots 0 and 1.  The activation loads are issued
+  // before any weight load of the workgroup (the first barrier); with
+  // `first` each wave then issues two granules of weights, which stream in
+  // while the parts are formed, and the rest of its ring after.
+  auto prepare = [&](int sp, bool first) {
+    constexpr int PPT = kSliceBits / kThreads;  // positions per thread
+    const int nt = sp + 1 <= sl_last ? 2 : 1;
+    float x[2][PPT][NB];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int j = 0; j < PPT; ++j) {
+        const int64_t k = (int64_t)(sp + t) * kSliceBits + j * kThreads + tid;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          const uint32_t off = (t < nt && k < K) ? static_cast<uint32_t>(((int64_t)b * K + k) * 4)
+                                                 : kNoLoad;
+          x[t][j][b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ares, off, 0, 0));
+        }
+      }
+    }
+    __syncthreads();                          // activations requested before any weight;
+                                              // nobody reads the old parts any more
+    if (first) {
+      ld_next_slice();
+#pragma unroll
+      for (int e = 0; e < kEarly; ++e) issue(wb[e]);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        float v = 0.f;
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) v = fmaxf(v, fabsf(x[t][j][b]));
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+        if (lane == 0) mx[t][wave][b] = v;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (t < nt) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          float v = 0.f;
+#pragma unroll
+          for (int i = 0; i < kWaves; ++i) v = fmaxf(v, mx[t][i][b]);
+          // scale 2^e with the largest |x| in [128, 256) (at most 2^119, so
+          // that every column scale stays a finite power of two); a zero
+          // slice keeps e = 0
+          int E = 0;
+          if (v > 0.f) (void)frexpf(v, &E);
+          const int e = v > 0.f ? min(8 - E, 119) : 0;
+          if (tid == 0) esc[t][b] = e;
+#pragma unroll
+          for (int j = 0; j < PPT; ++j) {
+            const float y0 = ldexpf(x[t][j][b], e);
+            const int q0 = __builtin_amdgcn_cvt_pk_fp8_f32(y0, 0.f, 0, false);
+            const float y1 = 16.f * (y0 - __builtin_amdgcn_cvt_f32_fp8(q0, 0));
+            const int q1 = __builtin_amdgcn_cvt_pk_fp8_f32(y1, 0.f, 0, false);
+            const float y2 = 16.f * (y1 - __builtin_amdgcn_cvt_f32_fp8(q1, 0));
+            const int q2 = __builtin_amdgcn_cvt_pk_fp8_f32(y2, 0.f, 0, false);
+            uint8_t* dst = parts[t] + part_offset(j * kThreads + tid, NCOL) + (3 * b) * 128;
+            dst[0] = static_cast<uint8_t>(q0);
+            dst[128] = static_cast<uint8_t>(q1);
+            dst[256] = static_cast<uint8_t>(q2);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (first) {
+#pragma unroll
+      for (int e = kEarly; e < DEPTH; ++e) issue(wb[e]);
+    }
+  };
+  prepare(sl_first, true);
+
+  int rnd = 0;
+  auto process_run = [&](auto tsel, int sl) {
+    constexpr int TI = decltype(tsel)::value;
+    const int a = run_a(sl);
+    const int n = run_b(sl) - a;
+    // this slice's B operands and scales
+    i32x8 bv[kSteps];
+    const uint8_t* src = parts[TI] + (col_c * 4 + G) * 32;
+#pragma unroll
+    for (int u = 0; u < kSteps; ++u) {
+      const uint4 y0 = *reinterpret_cast<const uint4*>(src + u * NCOL * 128);
+      const uint4 y1 = *reinterpret_cast<const uint4*>(src + u * NCOL * 128 + 16);
+      __builtin_memcpy(&bv[u], &y0, 16);
+      __builtin_memcpy(reinterpret_cast<char*>(&bv[u]) + 16, &y1, 16);
+    }
+    const int scl = 127 - esc[TI][cb] - 4 * cp;
+    const bool writer = col < NCOL && cp == 0;
+    float* pout = SPLIT ? partials + (((int64_t)a * sc.S + sl) * NB + cb) * kGranuleRows + 4 * G
+                        : out + (int64_t)cb * m + (int64_t)kGranuleRows * a + 4 * G;
+    const float* ps = s + (int64_t)kGranuleRows * a + 4 * G;
+    const int64_t pstep = SPLIT ? (int64_t)sc.S * NB * kGranuleRows : kGranuleRows;
+    for (int k0 = 0; k0 < n; k0 += DEPTH, ++rnd) {
+      if (ld_k >= ld_slots) ld_next_slice();
+#pragma unroll
+      for (int e = 0; e < DEPTH; ++e) {
+        if (k0 + e < n) {
+          const uint32_t wd[8] = {wb[e][0].x, wb[e][0].y, wb[e][0].z, wb[e][0].w,
+                                  wb[e][1].x, wb[e][1].y, wb[e][1].z, wb[e][1].w};
+          f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0;
+#pragma unroll
+          for (int u = 0; u < kSteps; u += 2) {
+            c0 = mfma(expand(wd[u]), bv[u], c0, scl);
+            c1 = mfma(expand(wd[u + 1]), bv[u + 1], c1, scl);
+          }
+          const f32x4 c = c0 + c1;
+          // the token's three part columns, in order: column 3b + p is
+          // lane r = 3b + p of the 16-lane row
+          float4 v;
+          v.x = -(c[0] + dpp_from<0x101>(c[0]) + dpp_from<0x102>(c[0]));
+          v.y = -(c[1] + dpp_from<0x101>(c[1]) + dpp_from<0x102>(c[1]));
+          v.z = -(c[2] + dpp_from<0x101>(c[2]) + dpp_from<0x102>(c[2]));
+          v.w = -(c[3] + dpp_from<0x101>(c[3]) + dpp_from<0x102>(c[3]));
+          if constexpr (SPLIT) {
+            if (writer) *reinterpret_cast<float4*>(pout) = v;
+          } else {
+            const int64_t row = (int64_t)kGranuleRows * (a + k0 + e) + 4 * G;
+            if (writer) {
+              if (row + 0 < m) pout[0] = ps[0] * v.x;
+              if (row + 1 < m) pout[1] = ps[1] * v.y;
+              if (row + 2 < m) pout[2] = ps[2] * v.z;
+              if (row + 3 < m) pout[3] = ps[3] * v.w;
+            }
+            ps += pstep;
+          }
+          pout += pstep;
+        }
+        issue(wb[e]);
+      }
+    }
+  };
+
+  for (int sl = sl_first; sl <= sl_last; ++sl) {
+    const int rel = sl - sl_first;
+    if (rel >= 2 && (rel & 1) == 0) prepare(sl, false);
+    if ((rel & 1) == 0)
+      process_run(std::integral_constant<int, 0>{}, sl);
+    else
+      process_run(std::integral_constant<int, 1>{}, sl);
+  }
+}
+
+// out[b][i] = s[i] * (sum over slices q of partials[i / 16][q][b][i % 16]),
+// in slice order: P lanes share a (row, token), lane part j adds slices j,
+// j + P, ... (at most 8 each, all loads in flight), then a fixed tree.
+template <int P>
+__global__ void __launch_bounds__(256) gemv_f4_reduce_kernel(const float* __restrict__ partials,
+                                                             const float* __restrict__ s,
+                                                             float* __restrict__ out, int64_t m,
+                                                             int S, int NB) {
+  constexpr int R = 64 / P;
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+  const int part = lane % P;
+  const int64_t idx = wave * R + lane / P;      // (token, row) = (idx / m, idx % m)
+  const int64_t b = idx / m;
+  const int64_t row = idx - b * m;
+  float sum = 0.f;
+  if (b < NB) {
+    const float* p = partials + ((row >> 4) * S * NB + b) * kGranuleRows + (row & 15);
+    const int64_t qstep = (int64_t)NB * kGranuleRows;
+    for (int q0 = part; q0 < S; q0 += 8 * P) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 + u * P;
+        v[u] = q < S ? p[(int64_t)q * qstep] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += v[u];
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < P; o <<= 1) sum += __shfl_xor(sum, o);
+  if (b < NB && part == 0) out[b * m + row] = s[row] * sum;
+}
+
+template <int P>
+void launch_reduce(const float* partials, const float* s, float* out, int64_t m, int S, int NB,
+                   hipStream_t st) {
+  constexpr int per_block = 4 * (64 / P);
+  const int64_t n = m * NB;
+  hipLaunchKernelGGL(gemv_f4_reduce_kernel<P>, dim3(static_cast<unsigned>((n + per_block - 1) / per_block)),
+                     dim3(256), 0, st, partials, s, out, m, S, NB);
+}
+
+void reduce_slices(const float* partials, const float* s, float* out, int64_t m, int S, int NB,
+                   hipStream_t st) {
+  const int need = (S + 7) / 8;
+  if (need <= 1) launch_reduce<1>(partials, s, out, m, S, NB, st);
+  else if (need <= 2) launch_reduce<2>(partials, s, out, m, S, NB, st);
+  else if (need <= 4) launch_reduce<4>(partials, s, out, m, S, NB, st);
+  else if (need <= 8) launch_reduce<8>(partials, s, out, m, S, NB, st);
+  else launch_reduce<16>(partials, s, out, m, S, NB, st);
+}
+
+Sched make_sched(int64_t m, int64_t K) {
+  Sched sc{};
+  sc.S = static_cast<int>((K + kSliceBits - 1) / kSliceBits);
+  sc.NG = (m + kGranuleRows - 1) / kGranuleRows;
+  sc.T = sc.NG * sc.S;
+  const int64_t gmax = (sc.T + kWaves - 1) / kWaves;
+  int cus = num_cus();
+  if (cus > kMaxGroups) cus = kMaxGroups;
+  sc.G = static_cast<int>(gmax < cus ? gmax : cus);
+  const double share = (double)sc.T / sc.G;
+  const double c = share < (double)sc.NG ? kStraddleCost * share : 0.0;
+  const double span = (double)sc.NG + c;
+  const double V = (double)sc.T + (sc.S - 1) * c;
+  for (int w = 0; w < sc.G; ++w) {
+    const double v = V * w / sc.G;
+    int64_t sl = (int64_t)(v / span);
+    if (sl >= sc.S) sl = sc.S - 1;
+    double off = v - sl * span;
+    if (off > (double)sc.NG) off = (double)sc.NG;
+    int64_t t = sl * sc.NG + (int64_t)(off + 1e-9);
+    if (t > sc.T) t = sc.T;
+    if (w > 0 && t < sc.start[w - 1]) t = sc.start[w - 1];
+    sc.start[w] = t;
+  }
+  sc.start[sc.G] = sc.T;
+  return sc;
+}
+
+template <int NB>
+hipError_t launch_nb(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
+                     const float* a_lift, float* out, void* ws, hipStream_t st) {
+  constexpr int DEPTH = kDepth;
+  const Sched sc = make_sched(m, K);
+  const uint32_t w_bytes = static_cast<uint32_t>(m * ldw * 4);
+  const uint32_t a_bytes = static_cast<uint32_t>(NB * K * 4);
+  if (sc.S == 1) {
+    hipLaunchKernelGGL((gemv_f4_kernel<NB, DEPTH, false>), dim3(sc.G), dim3(kThreads), 0, st, w,
+                       m, K, ldw, s, a_lift, out, nullptr, sc, w_bytes, a_bytes);
+    return hipGetLastError();
+  }
+  float* partials = static_cast<float*>(ws);
+  hipLaunchKernelGGL((gemv_f4_kernel<NB, DEPTH, true>), dim3(sc.G), dim3(kThreads), 0, st, w, m,
+                     K, ldw, s, a_lift, out, partials, sc, w_bytes, a_bytes);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  reduce_slices(partials, s, out, m, sc.S, NB, st);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t gemv_f4_workspace_bytes(int64_t m, int64_t K, int64_t B) {
+  const Sched sc = make_sched(m, K);
+  if (sc.S == 1) return 0;
+  return sizeof(float) * kGranuleRows * (size_t)sc.NG * sc.S * B;
+}
+
+hipError_t launch_gemv_f4(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
+                          const float* a_lift, int64_t B, float* out, void* ws, hipStream_t st) {
+  switch (B) {
+    case 1: return launch_nb<1>(w, m, K, ldw, s, a_lift, out, ws, st);
+    case 2: return launch_nb<2>(w, m, K, ldw, s, a_lift, out, ws, st);
+    case 3: return launch_nb<3>(w, m, K, ldw, s, a_lift, out, ws, st);
+    case 4: return launch_nb<4>(w, m, K, ldw, s, a_lift, out, ws, st);
+    default: return launch_nb<5>(w, m, K, ldw, s, a_lift, out, ws, st);
+  }
+}
+
+}  // namespace lq

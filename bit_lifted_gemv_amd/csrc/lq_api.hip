@@ -40,6 +40,21 @@ size_t dtype_size(lq_dtype dt) { return dt == LQ_F32 ? 4 : 2; }
 // lq_gemm addresses a 128-row or 128-token block with 32-bit buffer offsets
 constexpr int64_t kGemmMaxK = int64_t{1} << 22;
 
+// lq_gemv kernels by token count: one token on float16 activation-sum tables,
+// two to five on the float4-sign / float8-part matrix cores, six to sixteen
+// on the bfloat16 matrix cores.
+enum class GemvPath { kTables, kF4, kBf16 };
+GemvPath gemv_path(int64_t B) {
+  return B == 1 ? GemvPath::kTables : B <= 5 ? GemvPath::kF4 : GemvPath::kBf16;
+}
+size_t gemv_workspace(int64_t m, int64_t K, int64_t B) {
+  switch (gemv_path(B)) {
+    case GemvPath::kTables: return lq::gemv1_workspace_bytes(m, K);
+    case GemvPath::kF4: return lq::gemv_f4_workspace_bytes(m, K, B);
+    default: return lq::gemv_mfma_workspace_bytes(m, K, B);
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -275,7 +290,7 @@ lq_status lq_gemv_workspace_size(int64_t m, int64_t K, int64_t B, size_t* bytes)
   if (!bytes) return fail(LQ_ERR_NULL, "bytes is null");
   if (m < 1 || K < 1 || B < 1 || B > 16)
     return fail(LQ_ERR_SHAPE, "m=%lld K=%lld B=%lld", (long long)m, (long long)K, (long long)B);
-  *bytes = B == 1 ? lq::gemv1_workspace_bytes(m, K) : lq::gemv_mfma_workspace_bytes(m, K, B);
+  *bytes = gemv_workspace(m, K, B);
   return ok();
 }
 
@@ -305,20 +320,27 @@ lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw, c
   if (!aligned(w_packed, 16)) return fail(LQ_ERR_ALIGN, "w_packed must be 16-byte aligned");
   if (!aligned(a_lift, 16)) return fail(LQ_ERR_ALIGN, "a_lift must be 16-byte aligned");
   if (!aligned(s, 4) || !aligned(out, 4)) return fail(LQ_ERR_ALIGN, "misaligned s or out");
-  const size_t need = B == 1 ? lq::gemv1_workspace_bytes(m, K) : lq::gemv_mfma_workspace_bytes(m, K, B);
+  const size_t need = gemv_workspace(m, K, B);
   if (need > 0) {
     if (!workspace) return fail(LQ_ERR_WORKSPACE, "workspace of %zu bytes required", need);
     if (workspace_bytes < need)
       return fail(LQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
     if (!aligned(workspace, 256)) return fail(LQ_ERR_ALIGN, "workspace must be 256-byte aligned");
   }
-  if (B == 1)
-    return hip_status(lq::launch_gemv1(w_packed, m, K, ldw, s, a_lift, out, workspace,
-                                       as_stream(stream)),
-                      "lq_gemv launch");
-  return hip_status(lq::launch_gemv_mfma(w_packed, m, K, ldw, s, a_lift, B, out, workspace,
+  switch (gemv_path(B)) {
+    case GemvPath::kTables:
+      return hip_status(lq::launch_gemv1(w_packed, m, K, ldw, s, a_lift, out, workspace,
                                          as_stream(stream)),
-                    "lq_gemv launch");
+                        "lq_gemv launch");
+    case GemvPath::kF4:
+      return hip_status(lq::launch_gemv_f4(w_packed, m, K, ldw, s, a_lift, B, out, workspace,
+                                           as_stream(stream)),
+                        "lq_gemv launch");
+    default:
+      return hip_status(lq::launch_gemv_mfma(w_packed, m, K, ldw, s, a_lift, B, out, workspace,
+                                             as_stream(stream)),
+                        "lq_gemv launch");
+  }
 }
 
 lq_status lq_layer_b1_workspace_size(int64_t m, int64_t n, int32_t d, int32_t D,

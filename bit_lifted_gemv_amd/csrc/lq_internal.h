@@ -130,6 +130,12 @@ size_t gemv_mfma_workspace_bytes(int64_t m, int64_t K, int64_t B);
 hipError_t launch_gemv_mfma(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
                             const float* a_lift, int64_t B, float* out, void* ws, hipStream_t st);
 
+// Few-token GEMV on float4 sign / float8 activation-part matrix cores
+// (k_gemv_f4.hip), 1 <= B <= 5.
+size_t gemv_f4_workspace_bytes(int64_t m, int64_t K, int64_t B);
+hipError_t launch_gemv_f4(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
+                          const float* a_lift, int64_t B, float* out, void* ws, hipStream_t st);
+
 hipError_t launch_gemm(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
                        const void* a_lift, lq_dtype dt, int64_t B, float* out, hipStream_t st);
 

@@ -176,7 +176,7 @@ def lift_kron(a: torch.Tensor, s1: torch.Tensor, p1_inv: torch.Tensor, p2_inv: t
         out = torch.empty((B, K), dtype=out_dtype, device=a.device)
     nb = _sz(0)
     check(lib().lq_lift_kron_workspace_size(B, n, ctypes.byref(nb)))
-    ws = workspace(nb.value, a.device, -1)
+    ws = workspace(nb.value, a.device, -1, stream)
     check(lib().lq_lift_kron(_ptr(a), _dt(a), B, n, n1, _ptr(s1), _ptr(p1_inv), _ptr(p2_inv),
                              _ptr(s2), _ptr(M), d, D, _ptr(out), _dt(out), _ptr(ws), nb.value,
                              _stream(stream)))
@@ -204,7 +204,7 @@ def encode(w: torch.Tensor, M: torch.Tensor, A: Optional[torch.Tensor] = None,
         nb = _sz(0)
         check(lib().lq_encode_workspace_size(d, D, ctypes.byref(nb)))
         nbytes = nb.value
-        ws = workspace(nbytes, w.device, -2)
+        ws = workspace(nbytes, w.device, -2, stream)
     check(lib().lq_encode(_ptr(w), G, _ptr(M), _ptr(A), d, D, _ptr(codes), _ptr(err), _ptr(ws),
                           nbytes, _stream(stream)))
     return codes, err
@@ -222,7 +222,7 @@ def layer_b1(a: torch.Tensor, t_inv: torch.Tensor, M: torch.Tensor, d: int, D: i
         out = torch.empty((1, m), dtype=torch.float32, device=a.device)
     nb = _sz(0)
     check(lib().lq_layer_b1_workspace_size(m, n, d, D, ctypes.byref(nb)))
-    ws = workspace(nb.value, a.device, m) if nb.value else None
+    ws = workspace(nb.value, a.device, m, stream) if nb.value else None
     check(lib().lq_layer_b1(_ptr(a), _dt(a), n, _ptr(t_inv), _dt(t_inv), 128, _ptr(M), d, D,
                             _ptr(w_packed), m, ldw, _ptr(s), _ptr(out), _ptr(ws), nb.value,
                             _stream(stream)))
@@ -241,7 +241,7 @@ def gemm_decoded(w_packed: torch.Tensor, s: torch.Tensor, M: torch.Tensor, d: in
         out = torch.empty((B, m), dtype=torch.float32, device=u.device)
     nb = _sz(0)
     check(lib().lq_gemm_decoded_workspace_size(m, n, ctypes.byref(nb)))
-    ws = workspace(nb.value, u.device, -4)
+    ws = workspace(nb.value, u.device, -4, stream)
     check(lib().lq_gemm_decoded(_ptr(w_packed), m, n, ldw, _ptr(M), d, D, _ptr(s), _ptr(u),
                                 _dt(u), B, _ptr(out), _ptr(ws), nb.value, _stream(stream)))
     return out
@@ -261,7 +261,7 @@ def softmin_grad(w: torch.Tensor, M: torch.Tensor, T: float = 10.0,
         grad = torch.empty((d, D), dtype=torch.float32, device=w.device)
     nb = _sz(0)
     check(lib().lq_softmin_workspace_size(N, d, D, ctypes.byref(nb)))
-    ws = workspace(nb.value, w.device, -3)
+    ws = workspace(nb.value, w.device, -3, stream)
     check(lib().lq_softmin_grad(_ptr(w), N, _ptr(M), d, D, float(T), _ptr(loss), _ptr(grad),
                                 _ptr(ws), nb.value, _stream(stream)))
     return loss, grad
@@ -297,15 +297,16 @@ def learn_m(M0: torch.Tensor, batches, T: float = 10.0, lr: float = 0.01,
 _WS = {}
 
 
-def workspace(nbytes: int, device: torch.device, tag: int = 0) -> torch.Tensor:
-    """A workspace of at least nbytes, cached per (device, tag) and grown on
-    demand (the library needs no initialisation of its contents).  The GEMV
-    uses its row count as tag, the Kronecker lift -1, the encoder -2, the
-    soft-argmin objective -3, the decode-weights product -4."""
-    key = (device.type, device.index, tag)
+def workspace(nbytes: int, device: torch.device, tag: int = 0, stream=None) -> torch.Tensor:
+    """A workspace of at least nbytes, cached per (device, stream, tag) and
+    grown on demand, zero-filled when allocated.  Calls on one stream run in
+    order, so they may share it; calls on different streams get their own.
+    The GEMV uses its row count as tag, the Kronecker lift -1, the encoder -2,
+    the soft-argmin objective -3, the decode-weights product -4."""
+    key = (device.type, device.index, _stream(stream), tag)
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _WS[key] = ws
     return ws
 
@@ -323,10 +324,12 @@ def gemv(w_packed: torch.Tensor, s: torch.Tensor, a_lift: torch.Tensor, K: Optio
     m, ldw = w_packed.shape
     B, Ka = a_lift.shape
     K = Ka if K is None else K
+    if K != Ka:
+        raise ValueError(f"K={K} differs from the lifted activations' row length {Ka}")
     if out is None:
         out = torch.empty((B, m), dtype=torch.float32, device=a_lift.device)
     nws = gemv_workspace_size(m, K, B)
-    ws = workspace(nws, a_lift.device, m) if nws else None
+    ws = workspace(nws, a_lift.device, m, stream) if nws else None
     check(lib().lq_gemv(_ptr(w_packed), m, K, ldw, _ptr(s), _ptr(a_lift), B, _ptr(out), _ptr(ws),
                         nws, _stream(stream)))
     return out
@@ -339,6 +342,8 @@ def gemm(w_packed: torch.Tensor, s: torch.Tensor, a_lift: torch.Tensor, K: Optio
     m, ldw = w_packed.shape
     B, Ka = a_lift.shape
     K = Ka if K is None else K
+    if K != Ka:
+        raise ValueError(f"K={K} differs from the lifted activations' row length {Ka}")
     if out is None:
         out = torch.empty((B, m), dtype=torch.float32, device=a_lift.device)
     check(lib().lq_gemm(_ptr(w_packed), m, K, ldw, _ptr(s), _ptr(a_lift), _dt(a_lift), B,

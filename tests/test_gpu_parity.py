@@ -32,6 +32,13 @@ TOL_F32 = 1e-4
 # independent across the K/8 entries of a row, so the output error is about
 # 2^-11/sqrt(3) ~ 3e-4 of the output scale; 1e-3 keeps a 3x margin.
 TOL_LUT16 = 1e-3
+# With 2 <= B <= 5 each activation is carried by three float8 (E4M3) parts
+# of 4 significant bits each, every part kept in the normal range by a
+# power-of-two column scale per 1024-position slice: 12 significant bits,
+# a relative error of at most 2^-12 per value (less than 2^-17 of the
+# slice's largest value for the smallest ones), independent across K; the
+# products with +-1 are exact and summed in float32.  Measured 1.5e-5 to
+# 3e-5 on the workload shapes; the B >= 2 bar TOL_F32 covers it with margin.
 
 
 @pytest.fixture(scope="module")
@@ -199,6 +206,62 @@ def test_gemv_lifted_product(dev, m, K, B):
                   torch.from_numpy(al).to(dev), K).cpu().numpy()
     e = O.rel_err_colmax(got, ref)
     assert e <= (TOL_LUT16 if B == 1 else TOL_F32), e
+
+
+F4_CASES = [  # (m, K, B): 2..5 tokens on the float4-sign / float8-part matrix cores
+    (16, 1024, 2),      # one granule, one slice: no partial sums
+    (17, 1028, 3),      # a ragged row tile and a 4-position last slice
+    (1000, 4100, 5),    # five tokens (15 of 16 columns), ragged slices
+    (300, 20480, 4),    # a workgroup range over several slices
+    (64, 300000, 2),    # more slices than workgroups: ranges over > 2 slices
+    (4096, 10240, 3), (2050, 12288, 4),
+]
+
+
+@pytest.mark.parametrize("m,K,B", F4_CASES)
+def test_gemv_few_tokens_float8_parts(dev, m, K, B):
+    """2 <= B <= 5 on the float4 / float8 matrix cores, with outlier channels
+    (1 % x 20), a slice of zeros, and slices of tiny and huge activations (the
+    per-slice column scales keep every part normal)."""
+    _banner(f"gemv f4 m={m} K={K} B={B}")
+    rng = np.random.default_rng(m * 13 + K + B)
+    ldw = ((K + 31) // 32 + 3) // 4 * 4
+    packed = synth.random_sign_words(rng, m, K, ldw=ldw)
+    al = rng.standard_normal((B, K)).astype(np.float32)
+    al[:, rng.choice(K, size=max(1, K // 100), replace=False)] *= 20
+    if K > 3 * 1024:
+        al[0, 1024:2048] = 0
+        al[-1, 2048:3072] *= np.float32(1e-30)
+        al[0, 3072:4096] *= np.float32(1e25)
+    s = rng.uniform(0.01, 0.03, m).astype(np.float32)
+    got = lq.gemv(torch.from_numpy(packed.view(np.int32)).to(dev), torch.from_numpy(s).to(dev),
+                  torch.from_numpy(al).to(dev), K).cpu().numpy()
+    ref = O.lifted_product(packed, K, al, s)
+    e = O.rel_err_colmax(got, ref)
+    _banner(f"  rel err {e:.3e}")
+    assert np.isfinite(got).all()
+    assert e <= TOL_F32, e
+
+
+def test_gemv_few_tokens_scaling_is_exact(dev):
+    """2..5 tokens: the float8 parts are formed after a power-of-two scaling
+    chosen per slice, so scaling a token by 2^k scales its outputs by exactly
+    2^k, and the tokens do not affect each other."""
+    _banner("gemv f4 power-of-two scaling")
+    rng = np.random.default_rng(19)
+    m, K = 700, 5120
+    packed = synth.random_sign_words(rng, m, K)
+    w = torch.from_numpy(packed.view(np.int32)).to(dev)
+    sd = torch.from_numpy(rng.uniform(0.01, 0.03, m).astype(np.float32)).to(dev)
+    al = rng.standard_normal((4, K)).astype(np.float32)
+    base = lq.gemv(w, sd, torch.from_numpy(al).to(dev), K).cpu().numpy()
+    scaled = al.copy()
+    scaled[1] = np.ldexp(al[1], 60)
+    scaled[3] = np.ldexp(al[3], -60)
+    got = lq.gemv(w, sd, torch.from_numpy(scaled).to(dev), K).cpu().numpy()
+    assert np.array_equal(got[0], base[0]) and np.array_equal(got[2], base[2])
+    assert np.array_equal(got[1], np.ldexp(base[1], 60))
+    assert np.array_equal(got[3], np.ldexp(base[3], -60))
 
 
 @pytest.mark.parametrize("B", [1, 3])
