@@ -4,6 +4,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "lq_internal.h"
 
@@ -53,6 +54,69 @@ size_t gemv_workspace(int64_t m, int64_t K, int64_t B) {
     case GemvPath::kF4: return lq::gemv_f4_workspace_bytes(m, K, B);
     default: return lq::gemv_mfma_workspace_bytes(m, K, B);
   }
+}
+
+// Shape, pointer and alignment checks shared by lq_gemv and lq_gemv_noalloc.
+lq_status gemv_check(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw, const float* s,
+                     const float* a_lift, int64_t B, float* out) {
+  if (!w_packed || !s || !a_lift || !out) return fail(LQ_ERR_NULL, "null pointer");
+  if (m < 1 || K < 1) return fail(LQ_ERR_SHAPE, "m=%lld K=%lld", (long long)m, (long long)K);
+  if (B < 1 || B > 16) return fail(LQ_ERR_SHAPE, "B=%lld outside 1..16", (long long)B);
+  if (ldw < (K + 31) / 32) return fail(LQ_ERR_SHAPE, "ldw=%lld < ceil(K/32)", (long long)ldw);
+  if (ldw % 4) return fail(LQ_ERR_ALIGN, "ldw=%lld must be a multiple of 4", (long long)ldw);
+  if (K % 4) return fail(LQ_ERR_SHAPE, "K=%lld must be a multiple of 4", (long long)K);
+  // the kernels address weights and activations with 32-bit buffer offsets
+  if (m * ldw * 4 > ((int64_t)1 << 30))
+    return fail(LQ_ERR_SHAPE, "weights of %lld bytes exceed the 1 GiB per-call limit",
+                (long long)(m * ldw * 4));
+  if (K > ((int64_t)1 << 24))
+    return fail(LQ_ERR_SHAPE, "K=%lld exceeds the per-call limit of 2^24", (long long)K);
+  if (!aligned(w_packed, 16)) return fail(LQ_ERR_ALIGN, "w_packed must be 16-byte aligned");
+  if (!aligned(a_lift, 16)) return fail(LQ_ERR_ALIGN, "a_lift must be 16-byte aligned");
+  if (!aligned(s, 4) || !aligned(out, 4)) return fail(LQ_ERR_ALIGN, "misaligned s or out");
+  return LQ_OK;
+}
+
+lq_status gemv_launch(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw, const float* s,
+                      const float* a_lift, int64_t B, float* out, void* ws, hipStream_t st) {
+  switch (gemv_path(B)) {
+    case GemvPath::kTables:
+      return hip_status(lq::launch_gemv1(w_packed, m, K, ldw, s, a_lift, out, ws, st),
+                        "lq_gemv launch");
+    case GemvPath::kF4:
+      return hip_status(lq::launch_gemv_f4(w_packed, m, K, ldw, s, a_lift, B, out, ws, st),
+                        "lq_gemv launch");
+    default:
+      return hip_status(lq::launch_gemv_mfma(w_packed, m, K, ldw, s, a_lift, B, out, ws, st),
+                        "lq_gemv launch");
+  }
+}
+
+// Scratch of lq_gemv_noalloc: one array per GPU, in the code object, held
+// until the process ends.  Host code never uses the array's name as an
+// address: its device address is looked up once per device (with that
+// device current) and kept.  Every lq_gemv_noalloc call on a GPU shares it.
+constexpr size_t kScratchBytes = size_t{16} << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_pointer(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace
@@ -305,21 +369,8 @@ lq_status lq_workspace_clear(void* workspace, size_t bytes, void* stream) {
 lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw, const float* s,
                   const float* a_lift, int64_t B, float* out, void* workspace,
                   size_t workspace_bytes, void* stream) {
-  if (!w_packed || !s || !a_lift || !out) return fail(LQ_ERR_NULL, "null pointer");
-  if (m < 1 || K < 1) return fail(LQ_ERR_SHAPE, "m=%lld K=%lld", (long long)m, (long long)K);
-  if (B < 1 || B > 16) return fail(LQ_ERR_SHAPE, "B=%lld outside 1..16", (long long)B);
-  if (ldw < (K + 31) / 32) return fail(LQ_ERR_SHAPE, "ldw=%lld < ceil(K/32)", (long long)ldw);
-  if (ldw % 4) return fail(LQ_ERR_ALIGN, "ldw=%lld must be a multiple of 4", (long long)ldw);
-  if (K % 4) return fail(LQ_ERR_SHAPE, "K=%lld must be a multiple of 4", (long long)K);
-  // the kernel addresses weights and activations with 32-bit buffer offsets
-  if (m * ldw * 4 > ((int64_t)1 << 30))
-    return fail(LQ_ERR_SHAPE, "weights of %lld bytes exceed the 1 GiB per-call limit",
-                (long long)(m * ldw * 4));
-  if (K > ((int64_t)1 << 24))
-    return fail(LQ_ERR_SHAPE, "K=%lld exceeds the per-call limit of 2^24", (long long)K);
-  if (!aligned(w_packed, 16)) return fail(LQ_ERR_ALIGN, "w_packed must be 16-byte aligned");
-  if (!aligned(a_lift, 16)) return fail(LQ_ERR_ALIGN, "a_lift must be 16-byte aligned");
-  if (!aligned(s, 4) || !aligned(out, 4)) return fail(LQ_ERR_ALIGN, "misaligned s or out");
+  const lq_status st = gemv_check(w_packed, m, K, ldw, s, a_lift, B, out);
+  if (st != LQ_OK) return st;
   const size_t need = gemv_workspace(m, K, B);
   if (need > 0) {
     if (!workspace) return fail(LQ_ERR_WORKSPACE, "workspace of %zu bytes required", need);
@@ -327,20 +378,26 @@ lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw, c
       return fail(LQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
     if (!aligned(workspace, 256)) return fail(LQ_ERR_ALIGN, "workspace must be 256-byte aligned");
   }
-  switch (gemv_path(B)) {
-    case GemvPath::kTables:
-      return hip_status(lq::launch_gemv1(w_packed, m, K, ldw, s, a_lift, out, workspace,
-                                         as_stream(stream)),
-                        "lq_gemv launch");
-    case GemvPath::kF4:
-      return hip_status(lq::launch_gemv_f4(w_packed, m, K, ldw, s, a_lift, B, out, workspace,
-                                           as_stream(stream)),
-                        "lq_gemv launch");
-    default:
-      return hip_status(lq::launch_gemv_mfma(w_packed, m, K, ldw, s, a_lift, B, out, workspace,
-                                             as_stream(stream)),
-                        "lq_gemv launch");
+  return gemv_launch(w_packed, m, K, ldw, s, a_lift, B, out, workspace, as_stream(stream));
+}
+
+lq_status lq_gemv_noalloc(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw,
+                          const float* s, const float* a_lift, int64_t B, float* out,
+                          void* stream) {
+  const lq_status st = gemv_check(w_packed, m, K, ldw, s, a_lift, B, out);
+  if (st != LQ_OK) return st;
+  const size_t need = gemv_workspace(m, K, B);
+  if (need > kScratchBytes)
+    return fail(LQ_ERR_WORKSPACE,
+                "this shape needs %zu bytes of scratch, more than the %zu bytes the library "
+                "holds per GPU for lq_gemv_noalloc: use lq_gemv with a workspace",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = scratch_pointer(&ws);
+    if (e != hipSuccess) return hip_status(e, "lq_gemv_noalloc scratch address");
   }
+  return gemv_launch(w_packed, m, K, ldw, s, a_lift, B, out, ws, as_stream(stream));
 }
 
 lq_status lq_layer_b1_workspace_size(int64_t m, int64_t n, int32_t d, int32_t D,

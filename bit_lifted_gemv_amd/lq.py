@@ -28,7 +28,8 @@ EXPORTS = ("lq_status_string", "lq_last_error", "lq_version", "lq_pack_signs", "
            "lq_gemv_workspace_size", "lq_workspace_clear", "lq_gemv", "lq_gemm",
            "lq_encode_workspace_size", "lq_encode", "lq_softmin_workspace_size",
            "lq_softmin_grad", "lq_adam_update", "lq_gemm_decoded_workspace_size",
-           "lq_gemm_decoded", "lq_layer_b1_workspace_size", "lq_layer_b1")
+           "lq_gemm_decoded", "lq_layer_b1_workspace_size", "lq_layer_b1",
+           "lq_gemv_noalloc")
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -61,6 +62,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lq_workspace_clear": (_i32, [_vp, _sz, _vp]),
         "lq_gemv": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
         "lq_gemm": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _i32, _i64, _vp, _vp]),
+        "lq_gemv_noalloc": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp]),
         "lq_encode_workspace_size": (_i32, [_i32, _i32, ctypes.POINTER(_sz)]),
         "lq_encode": (_i32, [_vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
         "lq_softmin_workspace_size": (_i32, [_i64, _i32, _i32, ctypes.POINTER(_sz)]),
@@ -332,6 +334,18 @@ def gemv(w_packed: torch.Tensor, s: torch.Tensor, a_lift: torch.Tensor, K: Optio
     ws = workspace(nws, a_lift.device, m, stream) if nws else None
     check(lib().lq_gemv(_ptr(w_packed), m, K, ldw, _ptr(s), _ptr(a_lift), B, _ptr(out), _ptr(ws),
                         nws, _stream(stream)))
+    return out
+
+
+def gemv_noalloc(w_packed: torch.Tensor, s: torch.Tensor, a_lift: torch.Tensor,
+                 out: torch.Tensor, stream=None) -> torch.Tensor:
+    """lq_gemv without a workspace (the library's per-GPU scratch; calls on
+    one GPU must not overlap); out [B][m] float32 must be given."""
+    _dev(w_packed, s, a_lift, out)
+    m, ldw = w_packed.shape
+    B, K = a_lift.shape
+    check(lib().lq_gemv_noalloc(_ptr(w_packed), m, K, ldw, _ptr(s), _ptr(a_lift), B, _ptr(out),
+                                _stream(stream)))
     return out
 
 

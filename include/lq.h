@@ -277,6 +277,27 @@ lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * lq_gemv_noalloc -- lq_gemv for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments, kernels and result, without a workspace
+ * argument.  The partial sums go to a scratch array the library holds in its
+ * code object, one per GPU, LQ_GEMV_NOALLOC_MAX_BYTES bytes, kept until the
+ * process ends; its device address is looked up once per device on the
+ * first call there.  The call allocates nothing.
+ * Every lq_gemv_noalloc call on one GPU uses that GPU's one array: calls
+ * that may overlap on one GPU (other streams, other host threads) race and
+ * must be ordered by the caller.  Each call writes all of the scratch it
+ * reads, so no clearing is needed.
+ * Errors as lq_gemv; a shape whose lq_gemv_workspace_size exceeds
+ * LQ_GEMV_NOALLOC_MAX_BYTES returns LQ_ERR_WORKSPACE and launches nothing
+ * (every workload shape of 1 to 16 tokens up to 28672 x 68096 fits).
+ */
+#define LQ_GEMV_NOALLOC_MAX_BYTES (16u << 20)
+lq_status lq_gemv_noalloc(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw,
+                          const float* s, const float* a_lift, int64_t B, float* out,
+                          void* stream);
+
+/*
  * lq_layer_b1 -- the whole layer for one token, o = diag(s) W_q lift(T^-1 a)
  * (关键设计 4), with the lift computed inside the one-token product: each
  * workgroup of the weight stream computes the lifted activations of the

@@ -76,6 +76,24 @@ def test_gemv_workspace_required(L):
     assert L.lq_gemv_workspace_size(m, K, 1, None) == 1
 
 
+def test_gemv_noalloc_validation(L):
+    """The no-allocation GEMV checks like lq_gemv, and rejects a shape whose
+    workspace exceeds the library's scratch, all before any HIP call."""
+    assert L.lq_gemv_noalloc(None, 8, 64, 4, P, P, 1, P, None) == 1
+    assert L.lq_gemv_noalloc(P, 8, 64, 4, P, P, 17, P, None) == 2
+    assert L.lq_gemv_noalloc(P, 8, 66, 4, P, P, 1, P, None) == 2
+    assert L.lq_gemv_noalloc(MIS, 8, 64, 4, P, P, 1, P, None) == 4
+    n = ctypes.c_size_t(0)
+    m, K = 4096, 1 << 21               # 2048 slices: 32 MiB of partial sums
+    assert L.lq_gemv_workspace_size(m, K, 1, ctypes.byref(n)) == 0
+    assert n.value > (16 << 20)
+    assert L.lq_gemv_noalloc(P, m, K, K // 32, P, P, 1, P, None) == 7
+    assert "lq_gemv with a workspace" in _err(L)
+    for m, K, B in ((28672, 19456, 16), (8192, 68096, 16), (8192, 68096, 5), (8192, 68096, 1)):
+        assert L.lq_gemv_workspace_size(m, K, B, ctypes.byref(n)) == 0
+        assert n.value <= (16 << 20), (m, K, B, n.value)
+
+
 def test_lift_validation(L):
     F16, BF16 = lq.LQ_F16, lq.LQ_BF16
     ok = dict(B=1, n=1280, tb=128, d=10, D=24)
