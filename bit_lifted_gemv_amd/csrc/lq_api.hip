@@ -381,6 +381,16 @@ lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw, c
   return gemv_launch(w_packed, m, K, ldw, s, a_lift, B, out, workspace, as_stream(stream));
 }
 
+lq_status lq_stream_read(const void* buffer, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes == 0) return ok();
+  if (!buffer || !sink) return fail(LQ_ERR_NULL, "null pointer");
+  if (bytes % 16) return fail(LQ_ERR_SHAPE, "bytes=%zu must be a multiple of 16", bytes);
+  if (!aligned(buffer, 16) || !aligned(sink, 4)) return fail(LQ_ERR_ALIGN, "misaligned pointer");
+  return hip_status(lq::launch_stream_read(buffer, bytes, sink, 4 * lq::num_cus(),
+                                           as_stream(stream)),
+                    "lq_stream_read launch");
+}
+
 lq_status lq_gemv_noalloc(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw,
                           const float* s, const float* a_lift, int64_t B, float* out,
                           void* stream) {

@@ -113,6 +113,10 @@ hipError_t launch_lift_kron(const void* a, lq_dtype a_dt, int64_t B, int64_t n, 
                             const float* s2, const float* M, int d, int D, void* out,
                             lq_dtype out_dt, void* ws, hipStream_t st);
 
+// Plain streaming read (k_stream.hip): `groups` workgroups of 1024 threads.
+hipError_t launch_stream_read(const void* p, size_t bytes, uint32_t* sink, int groups,
+                              hipStream_t st);
+
 // Compute units of the current device (cached per device).
 int num_cus();
 

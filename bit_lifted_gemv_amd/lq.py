@@ -29,7 +29,7 @@ EXPORTS = ("lq_status_string", "lq_last_error", "lq_version", "lq_pack_signs", "
            "lq_encode_workspace_size", "lq_encode", "lq_softmin_workspace_size",
            "lq_softmin_grad", "lq_adam_update", "lq_gemm_decoded_workspace_size",
            "lq_gemm_decoded", "lq_layer_b1_workspace_size", "lq_layer_b1",
-           "lq_gemv_noalloc")
+           "lq_gemv_noalloc", "lq_stream_read")
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -63,6 +63,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lq_gemv": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp, _sz, _vp]),
         "lq_gemm": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _i32, _i64, _vp, _vp]),
         "lq_gemv_noalloc": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp]),
+        "lq_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
         "lq_encode_workspace_size": (_i32, [_i32, _i32, ctypes.POINTER(_sz)]),
         "lq_encode": (_i32, [_vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
         "lq_softmin_workspace_size": (_i32, [_i64, _i32, _i32, ctypes.POINTER(_sz)]),
@@ -347,6 +348,14 @@ def gemv_noalloc(w_packed: torch.Tensor, s: torch.Tensor, a_lift: torch.Tensor,
     check(lib().lq_gemv_noalloc(_ptr(w_packed), m, K, ldw, _ptr(s), _ptr(a_lift), B, _ptr(out),
                                 _stream(stream)))
     return out
+
+
+def stream_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read every byte of buf once (the HBM read-rate reference); sink: a
+    device int32 tensor of at least 4 x compute units."""
+    _dev(buf, sink)
+    check(lib().lq_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink),
+                               _stream(stream)))
 
 
 def gemm(w_packed: torch.Tensor, s: torch.Tensor, a_lift: torch.Tensor, K: Optional[int] = None,

@@ -277,6 +277,17 @@ lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * lq_stream_read -- a plain read of `bytes` bytes of device memory at
+ * `buffer` (16-byte aligned, bytes % 16 == 0), each byte once: the HBM read
+ * rate the one-token lq_gemv (which reads each weight byte once) is
+ * measured against.  sink: device uint32 [4 * compute units], caller-owned;
+ * written only in the unlikely case that the buffer's words fold to one
+ * fixed value (which keeps the loads from being removed).  Errors as the
+ * other calls; bytes == 0 is a no-op.
+ */
+lq_status lq_stream_read(const void* buffer, size_t bytes, uint32_t* sink, void* stream);
+
+/*
  * lq_gemv_noalloc -- lq_gemv for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): the same arguments, kernels and result, without a workspace

@@ -122,11 +122,16 @@ KRON_CASES = [  # (n, n1, d, D, B, act dtype): n2 = n / n1 <= 128, n2 % d == 0
     (1280, 16, 10, 24, 1, "f16"), (512, 4, 8, 20, 3, "bf16"), (8192, 64, 16, 40, 1, "bf16"),
     (8192, 64, 16, 40, 17, "f16"), (28672, 224, 8, 19, 1, "bf16"), (4096, 32, 8, 20, 5, "f32"),
     (384, 3, 4, 9, 2, "bf16"), (960, 12, 8, 16, 7, "bf16"), (6, 2, 3, 5, 1, "f32"),
-    # large batches: several column blocks per wave, a ragged last column slab
-    (8192, 64, 16, 40, 512, "bf16"), (2048, 16, 8, 19, 300, "f16"),
     # 64 tokens and more with small factors take the single-launch kernel:
-    # D % 4 != 0, float32 activations, several tokens per workgroup
+    # the prefill-scale shape, a ragged last token group, D % 4 != 0, float32
+    # activations, several tokens per workgroup
+    (8192, 64, 16, 40, 512, "bf16"), (2048, 16, 8, 19, 300, "f16"),
     (4096, 32, 8, 19, 70, "bf16"), (2048, 16, 4, 9, 65, "f16"), (1024, 16, 8, 20, 300, "f32"),
+    # 64 tokens and more that the single launch cannot take run the two
+    # launches with several column blocks per wave and a ragged last column
+    # slab: factors too large for LDS (n1 = 224), D > 64, d > 32
+    (28672, 224, 8, 19, 96, "bf16"), (8192, 64, 16, 80, 512, "bf16"),
+    (8192, 64, 64, 128, 100, "f16"),
 ]
 
 
