@@ -140,6 +140,12 @@ size_t gemv_f4_workspace_bytes(int64_t m, int64_t K, int64_t B);
 hipError_t launch_gemv_f4(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
                           const float* a_lift, int64_t B, float* out, void* ws, hipStream_t st);
 
+// One-launch GEMV for 1 <= B <= 5 (k_gemv_f4r.hip): each workgroup owns
+// whole rows; no workspace.  Applies when its LDS holds the sums.
+bool gemv_f4r_applies(int64_t m, int64_t K, int64_t B);
+hipError_t launch_gemv_f4r(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
+                           const float* a_lift, int64_t B, float* out, hipStream_t st);
+
 hipError_t launch_gemm(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
                        const void* a_lift, lq_dtype dt, int64_t B, float* out, hipStream_t st);
 

@@ -41,7 +41,7 @@ int main() {
   EXPECT(lq_gemv(W, int64_t{1} << 40, 64, 4, F, F, 1, O, nullptr, 0, nullptr), LQ_ERR_SHAPE);
   EXPECT(lq_gemv(W, 8, int64_t{1} << 40, int64_t{1} << 35, F, F, 1, O, nullptr, 0, nullptr),
          LQ_ERR_SHAPE);
-  EXPECT(lq_gemv(W, 28672, 19456, 608, F, F, 1, O, nullptr, 0, nullptr), LQ_ERR_WORKSPACE);
+  EXPECT(lq_gemv(W, 8192, 68096, 2128, F, F, 1, O, nullptr, 0, nullptr), LQ_ERR_WORKSPACE);
   EXPECT(lq_gemv_noalloc(W, 4096, 1 << 21, 1 << 16, F, F, 1, O, nullptr), LQ_ERR_WORKSPACE);
   EXPECT(lq_gemv_noalloc(nullptr, 8, 64, 4, F, F, 1, O, nullptr), LQ_ERR_NULL);
   size_t n = 0;

@@ -67,13 +67,22 @@ def test_gemv_validation(L):
 
 def test_gemv_workspace_required(L):
     n = ctypes.c_size_t(0)
-    m, K = 28672, 19456
+    m, K = 8192, 68096                 # 67 slices: too long for one workgroup's LDS
     assert L.lq_gemv_workspace_size(m, K, 1, ctypes.byref(n)) == 0
     assert n.value > 0, "this shape splits K and needs partial sums"
     assert L.lq_gemv(P, m, K, K // 32, P, P, 1, P, None, 0, None) == 7
     assert L.lq_gemv(P, m, K, K // 32, P, P, 1, P, P, n.value - 1, None) == 7
     assert L.lq_gemv_workspace_size(m, K, 0, ctypes.byref(n)) == 2
     assert L.lq_gemv_workspace_size(m, K, 1, None) == 1
+
+
+def test_gemv_one_launch_needs_no_workspace(L):
+    """Shapes whose every slice fits one workgroup's LDS take the one-launch
+    kernel: no workspace, and a null workspace is accepted."""
+    n = ctypes.c_size_t(1)
+    for m, K, B in ((28672, 19456, 1), (4096, 10240, 1), (1280, 3072, 5), (4096, 10240, 2)):
+        assert L.lq_gemv_workspace_size(m, K, B, ctypes.byref(n)) == 0
+        assert n.value == 0, (m, K, B)
 
 
 def test_gemv_noalloc_validation(L):

@@ -248,6 +248,43 @@ def test_gemv_few_tokens_float8_parts(dev, m, K, B):
     assert e <= TOL_F32, e
 
 
+ROWS_CASES = [  # (m, K, B) on the one-launch kernel (every slice in one workgroup's LDS)
+    (1, 4, 1),          # one row, one 4-position slice
+    (4100, 40960, 1),   # 40 slices, the most one token takes; a last workgroup of one row tile
+    (4097, 3072, 1),    # a ragged last row tile of one row
+    (300, 16384, 2),    # 16 slices, the most two tokens take
+    (33, 7200, 3),      # a ragged last slice
+    (1000, 8192, 5),    # 8 slices, the most five tokens take
+    (16, 1024, 4),      # one granule
+]
+
+
+@pytest.mark.parametrize("m,K,B", ROWS_CASES)
+def test_gemv_one_launch(dev, m, K, B):
+    """The one-launch kernel (no workspace) at its boundaries, with the same
+    outliers, zero slice and tiny / huge slices as the slice-major cases; the
+    precision is that of the float8 parts for every token count."""
+    _banner(f"gemv one-launch m={m} K={K} B={B}")
+    assert lq.gemv_workspace_size(m, K, B) == 0, "shape expected on the one-launch kernel"
+    rng = np.random.default_rng(m * 11 + K + B)
+    ldw = ((K + 31) // 32 + 3) // 4 * 4
+    packed = synth.random_sign_words(rng, m, K, ldw=ldw)
+    al = rng.standard_normal((B, K)).astype(np.float32)
+    al[:, rng.choice(K, size=max(1, K // 100), replace=False)] *= 20
+    if K > 3 * 1024:
+        al[0, 1024:2048] = 0
+        al[-1, 2048:3072] *= np.float32(1e-30)
+        al[0, 3072:4096] *= np.float32(1e25)
+    s = rng.uniform(0.01, 0.03, m).astype(np.float32)
+    got = lq.gemv(torch.from_numpy(packed.view(np.int32)).to(dev), torch.from_numpy(s).to(dev),
+                  torch.from_numpy(al).to(dev), K).cpu().numpy()
+    ref = O.lifted_product(packed, K, al, s)
+    e = O.rel_err_colmax(got, ref)
+    _banner(f"  rel err {e:.3e}")
+    assert np.isfinite(got).all()
+    assert e <= TOL_F32, e
+
+
 def test_gemv_few_tokens_scaling_is_exact(dev):
     """2..5 tokens: the float8 parts are formed after a power-of-two scaling
     chosen per slice, so scaling a token by 2^k scales its outputs by exactly
