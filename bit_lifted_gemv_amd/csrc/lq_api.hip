@@ -252,28 +252,31 @@ lq_status lq_gemm_decoded(const uint32_t* w_packed, int64_t m, int64_t n, int64_
                           const float* M, int32_t d, int32_t D, const float* s, const void* u,
                           lq_dtype u_dtype, int64_t B, float* out, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  if (!w_packed || !M || !s || !u || !out || !workspace) return fail(LQ_ERR_NULL, "null pointer");
+  if (!w_packed || !M || !s || !u || !out) return fail(LQ_ERR_NULL, "null pointer");
   if (u_dtype != LQ_F16) return fail(LQ_ERR_DTYPE, "u must be LQ_F16");
   if (m < 1 || n < 1 || B < 1 || m > INT32_MAX || n > INT32_MAX || B > INT32_MAX)
     return fail(LQ_ERR_SHAPE, "m=%lld n=%lld B=%lld", (long long)m, (long long)n, (long long)B);
+  // a workgroup addresses 128 tokens of u and 128 rows of signs with 32-bit
+  // buffer offsets
+  if (n > (int64_t{1} << 22))
+    return fail(LQ_ERR_SHAPE, "n=%lld exceeds the per-call limit of 2^22", (long long)n);
   if (d < 1 || d > 64 || D < 1 || D > 256 || n % d)
     return fail(LQ_ERR_SHAPE, "d=%d D=%d n=%lld (1 <= d <= 64, 1 <= D <= 256, n %% d == 0)",
                 (int)d, (int)D, (long long)n);
   const int64_t K = n / d * D;
   if (ldw < (K + 31) / 32) return fail(LQ_ERR_SHAPE, "ldw=%lld < ceil(K/32)", (long long)ldw);
+  if (ldw > (int64_t{1} << 22))
+    return fail(LQ_ERR_SHAPE, "ldw=%lld exceeds the per-call limit of 2^22", (long long)ldw);
   if (!lq::gemm_decoded_shape_ok(d, D))
     return fail(LQ_ERR_UNSUPPORTED, "d=%d D=%d beyond the decode tiles", (int)d, (int)D);
   if (workspace_bytes < lq::gemm_decoded_workspace_bytes(m, n))
     return fail(LQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes,
                 lq::gemm_decoded_workspace_bytes(m, n));
-  if (!aligned(workspace, 256)) return fail(LQ_ERR_ALIGN, "workspace must be 256-byte aligned");
   if (!aligned(w_packed, 4) || !aligned(M, 4) || !aligned(s, 4) || !aligned(u, 2) ||
       !aligned(out, 4))
     return fail(LQ_ERR_ALIGN, "misaligned pointer");
-  const char* why = nullptr;
   const hipError_t e = lq::launch_gemm_decoded(w_packed, m, n, ldw, M, d, D, s, u, B, out,
-                                               workspace, as_stream(stream), &why);
-  if (why) return fail(LQ_ERR_HIP, "lq_gemm_decoded: %s", why);
+                                               workspace, as_stream(stream), nullptr);
   return hip_status(e, "lq_gemm_decoded launch");
 }
 

@@ -89,8 +89,8 @@ hipError_t launch_lift_mfma(const void* a, lq_dtype dt, int64_t B, int64_t n, co
 
 // Lift with the Kronecker-factored whitening (k_lift_kron.hip).
 bool lift_kron_shape_ok(int64_t n, int n1, int d, int D);
+// Decode-weights product, one kernel (k_gemm_dec.hip); no workspace.
 bool gemm_decoded_shape_ok(int d, int D);
-int64_t gemm_decoded_chunk_rows(int64_t m, int64_t n);
 size_t gemm_decoded_workspace_bytes(int64_t m, int64_t n);
 hipError_t launch_gemm_decoded(const uint32_t* w, int64_t m, int64_t n, int64_t ldw,
                                const float* M, int d, int D, const float* s, const void* u,

@@ -244,9 +244,10 @@ def gemm_decoded(w_packed: torch.Tensor, s: torch.Tensor, M: torch.Tensor, d: in
         out = torch.empty((B, m), dtype=torch.float32, device=u.device)
     nb = _sz(0)
     check(lib().lq_gemm_decoded_workspace_size(m, n, ctypes.byref(nb)))
-    ws = workspace(nb.value, u.device, -4, stream)
+    ws = workspace(nb.value, u.device, -4, stream) if nb.value else None
     check(lib().lq_gemm_decoded(_ptr(w_packed), m, n, ldw, _ptr(M), d, D, _ptr(s), _ptr(u),
-                                _dt(u), B, _ptr(out), _ptr(ws), nb.value, _stream(stream)))
+                                _dt(u), B, _ptr(out), _ptr(ws) if ws is not None else None,
+                                nb.value, _stream(stream)))
     return out
 
 

@@ -171,24 +171,23 @@ lq_status lq_encode(const float* w, int64_t groups, const float* M, const float*
  * sum_j M[r][j] sigma_{i, g*D + j} (w = M y, 关键设计 1), then
  *   out[b][i] = s[i] * sum_{k<n} W_hat[i][k] * u[b][k],
  * the same linear map as lq_gemm on the lifted activations (y . (M^T x) =
- * (M y) . x), at 2 m n B + 2 m n D flops instead of 2 m K B (fewer once
- * B > D d / (D - d)).
+ * (M y) . x), at 2 m n B flops for the product plus the reconstruction,
+ * instead of 2 m K B (fewer once B > D d / (D - d)).
  * w_packed: uint32 [m][ldw] (layout of lq_pack_signs), ldw >= ceil(K/32),
  *           K = n*D/d.
  * M:        float [d][D];  s: float [m].
  * u:        float16 [B][n], the whitened activations T^-1 a (for example
  *           lq_lift_activations with M = I_4, d = D = 4).
  * out:      float [B][m].
- * workspace: >= lq_gemm_decoded_workspace_size bytes (the decoded weights of
- *           a chunk of rows, float16, s folded in), 256-byte aligned,
- *           caller-owned, no initialisation needed.
- * Arithmetic: the weights are decoded on the matrix cores from M rounded to
- * float16 (exact +-1 signs, float32 sums), scaled by s[i] and rounded to
- * float16 (relative 2^-11 each); u in float16; the product sums in float32
- * (rocBLAS GEMM).
- * Requires n % d == 0, 1 <= d <= 64, 1 <= D <= 256, m, n, B <= 2^31 - 1; u
- * must be LQ_F16 (else LQ_ERR_DTYPE).  A rocBLAS failure is reported as LQ_ERR_HIP.  The rocBLAS
- * handle is created per device and host thread on first use.
+ * workspace: none is needed (lq_gemm_decoded_workspace_size gives 0); the
+ *           pointer may be null.
+ * Arithmetic: one kernel reconstructs the weights on the matrix cores from
+ * M rounded to float16 (exact +-1 signs, float32 sums), rounds them to
+ * float16 (relative 2^-11) and contracts them with u on the matrix cores in
+ * float32; s[i] scales the float32 result.  The weights never leave the
+ * chip.
+ * Requires n % d == 0, 1 <= d <= 64, 1 <= D <= 256, n <= 2^22, ldw <= 2^22,
+ * m, B <= 2^31 - 1; u must be LQ_F16 (else LQ_ERR_DTYPE).
  */
 lq_status lq_gemm_decoded_workspace_size(int64_t m, int64_t n, size_t* bytes);
 lq_status lq_gemm_decoded(const uint32_t* w_packed, int64_t m, int64_t n, int64_t ldw,

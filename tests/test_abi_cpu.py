@@ -208,23 +208,24 @@ def test_softmin_and_adam_validation(L):
 
 def test_gemm_decoded_validation(L):
     nb = ctypes.c_size_t(0)
+    nb.value = 1
     assert L.lq_gemm_decoded_workspace_size(8192, 8192, ctypes.byref(nb)) == 0
-    assert nb.value >= 2 * 8192 * 16 and nb.value % 256 == 0
+    assert nb.value == 0, "the decoded weights stay on chip: no workspace"
     F16, BF16 = lq.LQ_F16, lq.LQ_BF16
 
-    def call(w=P, m=64, n=512, ldw=40, M=P, d=16, D=40, s=P, u=P, udt=F16, B=8, out=P, ws=P,
-             wsb=1 << 30):
+    def call(w=P, m=64, n=512, ldw=40, M=P, d=16, D=40, s=P, u=P, udt=F16, B=8, out=P, ws=None,
+             wsb=0):
         return L.lq_gemm_decoded(w, m, n, ldw, M, d, D, s, u, udt, B, out, ws, wsb, None)
 
     assert call(w=None) == 1
-    assert call(ws=None) == 1
+    assert call(u=None) == 1
     assert call(udt=BF16) == 3
     assert call(n=500) == 2                  # n % d
     assert call(ldw=39) == 2                 # K = 1280 needs 40 words
     assert call(d=65, n=520, ldw=64) == 2    # d > 64
+    assert call(D=257) == 2                  # D > 256
     assert call(B=0) == 2
-    assert call(wsb=16) == 7
-    assert call(ws=P + 2) == 4
+    assert call(n=(1 << 22) + 16, ldw=(1 << 22) * 5 // 64 + 8) == 2   # 32-bit offsets
     assert call(u=P + 1) == 4
 
 

@@ -3,11 +3,11 @@ ABI) against the float64 oracle's dense route (o = s * (W_hat T^-1 a), which
 is this product written out).
 
 Bar: the layer tolerance 2e-3 (e = max over tokens of max_i |o - o_ref| /
-max_i |o_ref|).  The decoded weights s_i W_hat are rounded once to float16
-(relative 2^-11) and u = T^-1 a once to float16 (2^-11) after the 16-bit
-input's own rounding; summed in float32 over n independent terms, the
-output error is about 2^-11 * sqrt(2/3) ~ 4e-4 of the output scale, so
-2e-3 keeps a 5x margin."""
+max_i |o_ref|).  The decoded weights W_hat are rounded once to float16
+(relative 2^-11; s is applied to the float32 sums) and u = T^-1 a once to
+float16 (2^-11) after the 16-bit input's own rounding; summed in float32
+over n independent terms, the output error is about 2^-11 * sqrt(2/3) ~
+4e-4 of the output scale, so 2e-3 keeps a 5x margin."""
 import numpy as np
 import pytest
 import torch
@@ -70,9 +70,9 @@ def test_decoded_lq40_16_full_size_sampled(dev):
     assert e <= TOL, e
 
 
-def test_decoded_chunks_rows(dev):
-    """More rows than one decode chunk (2^27 weights / n rows each): the
-    product runs chunk by chunk into the right output columns."""
+def test_decoded_many_row_tiles(dev):
+    """Many 64-row workgroup tiles (and a ragged last one) with a few
+    tokens: every tile's rows land in the right output columns."""
     m, n, d, D, B = 2 * (1 << 27) // 4096 + 48, 4096, 8, 16, 24
     print(f"decoded chunked m={m} n={n}", flush=True)
     L = synth.make_layer(m, n, d, D, B, seed=5, dtype="bf16")
