@@ -696,23 +696,4 @@ size_t gemv1_workspace_bytes(int64_t m, int64_t K) {
   return sizeof(float) * kGranuleRows * (size_t)sc.NG * sc.S;
 }
 
-hipError_t launch_gemv1(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
-                        const float* a_lift, float* out, void* ws, hipStream_t st) {
-  const Sched1 sc = make_sched1(m, K);
-  const uint32_t w_bytes = static_cast<uint32_t>(m * ldw * 4);
-  const uint32_t a_bytes = static_cast<uint32_t>(K * 4);
-  if (sc.S == 1) {
-    hipLaunchKernelGGL((gemv1_kernel<false, -1>), dim3(sc.G), dim3(kThreads), 0, st, w, m, K,
-                       ldw, s, a_lift, out, nullptr, sc, w_bytes, a_bytes, LiftIn{});
-  } else {
-    float* partials = static_cast<float*>(ws);
-    hipLaunchKernelGGL((gemv1_kernel<true, -1>), dim3(sc.G), dim3(kThreads), 0, st, w, m, K,
-                       ldw, s, a_lift, out, partials, sc, w_bytes, a_bytes, LiftIn{});
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    reduce_slices(partials, s, out, m, sc.S, st);
-  }
-  return hipGetLastError();
-}
-
 }  // namespace lq

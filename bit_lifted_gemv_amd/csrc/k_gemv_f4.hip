@@ -4,49 +4,32 @@
 // (LiftQuant notes, 关键设计 4: after the activation transform the layer is a
 // product of 1-bit weights with floats, scaled per row by s).
 //
-// Operands of v_mfma_scale_f32_16x16x128_f8f6f4.  A (16 rows x 128 lifted
-// positions) holds the signs as float4 (E2M1) values +-1: from a word of 32
-// sign bits, dword q of the lane's operand takes bits q, q + 4, ..., q + 28
-// (nibble t <- bit 4 t + q), so each dword is one shift and one bit-field
-// insert; a set bit gives -1 (the products carry -sigma and the partial sums
-// are negated back).  B (128 positions x 16 columns) holds the activations of
-// up to five tokens as three float8 (E4M3) parts each, in columns 3 b + p:
-// for each 1024-position slice and token, x is scaled by 2^e (e puts the
-// slice's largest |x| in [128, 256)), then p0 = fp8(x 2^e), p1 = fp8(16 r0),
-// p2 = fp8(16 r1) with r the remainders (exact in float32); the hardware
-// scale of column (b, p) is 2^(-e - 4 p), so the three columns of a token add
-// up to x with a relative error of about 2^-12 of the slice's largest
-// |x| at worst.  Products are exact and accumulate in float32.
-//
-// Position order.  Each 1024-position slice of a row is 128 bytes; lane
-// (r, G) of a 16-row tile loads bytes 16 G .. 16 G + 15 and 64 + 16 G ..
-// 64 + 16 G + 15 of row r (words 4 G + u and 16 + 4 G + u, u < 4).  MFMA
-// step u < 4 takes word 4 G + u from lane group G, step 4 + u word
-// 16 + 4 G + u.  Within a word, bit 4 t + q sits at A slot 8 q + t, which in
-// the float8 B operand is lane group (32 G + 8 q + t) % 64 / 16, byte
-// (8 q + t) % 16 + 16 G / 2 (the float8 operand holds positions 16 g ..
-// 16 g + 15 and 64 + 16 g .. 64 + 16 g + 15 of the step); the activation
-// parts are stored in that order.
+// Matrix-core operands as in f4_parts.h: sign bits as float4 (A) masked in
+// place, each activation as three float8 parts in B columns 3 b + p with a
+// power-of-two hardware scale per 1024-position slice; a slice contributes
+// 2 R - sum a, with R the sum of the activations whose bit is set.
 //
 // Work split (as the one-token table kernel): granule = 16 rows x one slice;
 // granules ordered (slice, row) and cut into one range per workgroup (one
 // workgroup of 8 waves per CU); each wave streams a contiguous run of
 // granules per slice with a ring of DEPTH granules of loads in flight.  At
 // the start of a slice the workgroup turns the slice's activations into the
-// float8 parts (in LDS), and each wave keeps the B operands of the slice's 8
-// steps in registers while it streams the slice's granules.  Each granule
+// float8 parts (in LDS; one wave converts a slice, 16 positions per lane),
+// and each wave keeps the B operands of the slice's 8 steps in registers
+// while it streams the slice's granules.  Each granule
 // leaves the 16 rows' sums of one slice per token in the workspace; a second
 // kernel adds each row's S partial sums in slice order, scales by s and
 // writes the row.  Deterministic.
 #include <type_traits>
 
+#include "f4_parts.h"
 #include "lq_internal.h"
 
 namespace lq {
 namespace {
 
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+using f4::f32x4;
+using f4::i32x8;
 
 constexpr int kSliceBits = 1024;
 constexpr int kSliceBytes = kSliceBits / 8;     // 128 bytes of a row per slice
@@ -68,42 +51,6 @@ struct Sched {
   int64_t start[kMaxGroups + 1];
 };
 
-// A operand from one word of 32 signs: dword q, nibble t <- bit 4 t + q;
-// bit 1 -> 0xA (-1.0), bit 0 -> 0x2 (+1.0).
-__device__ __forceinline__ i32x8 expand(uint32_t w) {
-  i32x8 a;
-  a[0] = static_cast<int>(((w << 3) & 0x88888888u) | 0x22222222u);
-  a[1] = static_cast<int>(((w << 2) & 0x88888888u) | 0x22222222u);
-  a[2] = static_cast<int>(((w << 1) & 0x88888888u) | 0x22222222u);
-  a[3] = static_cast<int>((w & 0x88888888u) | 0x22222222u);
-  a[4] = a[5] = a[6] = a[7] = 0;               // unused with a float4 A operand
-  return a;
-}
-
-__device__ __forceinline__ f32x4 mfma(const i32x8& a, const i32x8& b, const f32x4& c, int sc) {
-  // A: E2M1 (cbsz 4), scale 2^0; B: E4M3 (blgp 0), scale 2^(sc - 127)
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, 127, 0, sc);
-}
-
-// Byte offset, within a slice's parts, of position k (< 1024) for column
-// 0 and lane-group byte (the column adds 128 bytes each): step-major
-// [step][column][lane group][32 bytes].
-__device__ __forceinline__ int part_offset(int k, int ncol) {
-  const int w = k >> 5, bit = k & 31;
-  const int u = w < 16 ? (w & 3) : 4 + ((w - 16) & 3);
-  const int G = w < 16 ? (w >> 2) : ((w - 16) >> 2);
-  const int slot = 8 * (bit & 3) + (bit >> 2);
-  const int kap = 32 * G + slot;
-  const int g = (kap & 63) >> 4;
-  const int beta = (kap & 15) + (kap >= 64 ? 16 : 0);
-  return (u * ncol * 4 + g) * 32 + beta;
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_from(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
 // NB: tokens (1..5); DEPTH: granules of weights in flight per wave.
 template <int NB, int DEPTH, bool SPLIT>
 __global__ void __launch_bounds__(kThreads, 1) gemv_f4_kernel(
@@ -111,10 +58,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_f4_kernel(
     const float* __restrict__ s, const float* __restrict__ ah, float* __restrict__ out,
     float* __restrict__ partials, Sched sc, uint32_t w_bytes, uint32_t a_bytes) {
   constexpr int NCOL = 3 * NB;
-  constexpr int kPartBytes = kSteps * NCOL * 4 * 32;          // per slice
+  constexpr int kPartBytes = f4::part_bytes(NB);               // per slice
   __shared__ __attribute__((aligned(16))) uint8_t parts[2][kPartBytes];
-  __shared__ float mx[2][kWaves][NB];
   __shared__ int esc[2][NB];
+  __shared__ float asum[2][NB];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -189,24 +136,25 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_f4_kernel(
   };
 
   // Activation parts of slices sp and sp + 1 (the second if the range
-  // reaches it) into LDS slots 0 and 1.  The activation loads are issued
-  // before any weight load of the workgroup (the first barrier); with
-  // `first` each wave then issues two granules of weights, which stream in
-  // while the parts are formed, and the rest of its ring after.
-  auto prepare = [&](int sp, bool first) {
-    constexpr int PPT = kSliceBits / kThreads;  // positions per thread
+  // reaches it) into LDS slots 0 and 1, wave t converting slice sp + t.  The
+  // activation loads are issued before any weight load of the workgroup (the
+  // first barrier); with `first` each wave then issues two granules of
+  // weights, which stream in while the parts are formed, and the rest of its
+  // ring after.
+  auto prepare = [&](int sp, bool first) __attribute__((always_inline)) {
     const int nt = sp + 1 <= sl_last ? 2 : 1;
-    float x[2][PPT][NB];
+    const bool conv = wave < nt;                // uniform
+    f32x4 xv[NB][4];
+    if (conv) {
+      const int64_t k0 = (int64_t)(sp + wave) * kSliceBits + 16 * lane;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int b = 0; b < NB; ++b) {
 #pragma unroll
-      for (int j = 0; j < PPT; ++j) {
-        const int64_t k = (int64_t)(sp + t) * kSliceBits + j * kThreads + tid;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const uint32_t off = (t < nt && k < K) ? static_cast<uint32_t>(((int64_t)b * K + k) * 4)
-                                                 : kNoLoad;
-          x[t][j][b] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(ares, off, 0, 0));
+        for (int c = 0; c < 4; ++c) {
+          const int64_t k = k0 + 4 * c;         // K % 4 == 0: all four or none
+          const uint32_t off = k < K ? static_cast<uint32_t>(((int64_t)b * K + k) * 4) : kNoLoad;
+          const auto v = __builtin_amdgcn_raw_buffer_load_b128(ares, off, 0, 0);
+          __builtin_memcpy(&xv[b][c], &v, 16);
         }
       }
     }
@@ -217,49 +165,20 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_f4_kernel(
 #pragma unroll
       for (int e = 0; e < kEarly; ++e) issue(wb[e]);
     }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    if (conv) {
+      uint32_t mb[NB];
+      float sum[NB];
+      f4::slice_stats<NB>(xv, mb, sum);
+      int e[NB];
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        float v = 0.f;
-#pragma unroll
-        for (int j = 0; j < PPT; ++j) v = fmaxf(v, fabsf(x[t][j][b]));
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-        if (lane == 0) mx[t][wave][b] = v;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (t < nt) {
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          float v = 0.f;
-#pragma unroll
-          for (int i = 0; i < kWaves; ++i) v = fmaxf(v, mx[t][i][b]);
-          // scale 2^e with the largest |x| in [128, 256) (at most 2^119, so
-          // that every column scale stays a finite power of two); a zero
-          // slice keeps e = 0
-          int E = 0;
-          if (v > 0.f) (void)frexpf(v, &E);
-          const int e = v > 0.f ? min(8 - E, 119) : 0;
-          if (tid == 0) esc[t][b] = e;
-#pragma unroll
-          for (int j = 0; j < PPT; ++j) {
-            const float y0 = ldexpf(x[t][j][b], e);
-            const int q0 = __builtin_amdgcn_cvt_pk_fp8_f32(y0, 0.f, 0, false);
-            const float y1 = 16.f * (y0 - __builtin_amdgcn_cvt_f32_fp8(q0, 0));
-            const int q1 = __builtin_amdgcn_cvt_pk_fp8_f32(y1, 0.f, 0, false);
-            const float y2 = 16.f * (y1 - __builtin_amdgcn_cvt_f32_fp8(q1, 0));
-            const int q2 = __builtin_amdgcn_cvt_pk_fp8_f32(y2, 0.f, 0, false);
-            uint8_t* dst = parts[t] + part_offset(j * kThreads + tid, NCOL) + (3 * b) * 128;
-            dst[0] = static_cast<uint8_t>(q0);
-            dst[128] = static_cast<uint8_t>(q1);
-            dst[256] = static_cast<uint8_t>(q2);
-          }
+        e[b] = f4::slice_exponent(mb[b]);
+        if (lane == 0) {
+          esc[wave][b] = e[b];
+          asum[wave][b] = sum[b];
         }
       }
+      f4::slice_parts<NB>(xv, e, parts[wave], lane);
     }
     __syncthreads();
     if (first) {
@@ -285,6 +204,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_f4_kernel(
       __builtin_memcpy(reinterpret_cast<char*>(&bv[u]) + 16, &y1, 16);
     }
     const int scl = 127 - esc[TI][cb] - 4 * cp;
+    const float asl = asum[TI][cb];
     const bool writer = col < NCOL && cp == 0;
     float* pout = SPLIT ? partials + (((int64_t)a * sc.S + sl) * NB + cb) * kGranuleRows + 4 * G
                         : out + (int64_t)cb * m + (int64_t)kGranuleRows * a + 4 * G;
@@ -300,17 +220,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_f4_kernel(
           f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0;
 #pragma unroll
           for (int u = 0; u < kSteps; u += 2) {
-            c0 = mfma(expand(wd[u]), bv[u], c0, scl);
-            c1 = mfma(expand(wd[u + 1]), bv[u + 1], c1, scl);
+            c0 = f4::mfma(f4::expand(wd[u]), bv[u], c0, scl);
+            c1 = f4::mfma(f4::expand(wd[u + 1]), bv[u + 1], c1, scl);
           }
           const f32x4 c = c0 + c1;
-          // the token's three part columns, in order: column 3b + p is
-          // lane r = 3b + p of the 16-lane row
           float4 v;
-          v.x = -(c[0] + dpp_from<0x101>(c[0]) + dpp_from<0x102>(c[0]));
-          v.y = -(c[1] + dpp_from<0x101>(c[1]) + dpp_from<0x102>(c[1]));
-          v.z = -(c[2] + dpp_from<0x101>(c[2]) + dpp_from<0x102>(c[2]));
-          v.w = -(c[3] + dpp_from<0x101>(c[3]) + dpp_from<0x102>(c[3]));
+          v.x = f4::slice_sum(c[0], asl);
+          v.y = f4::slice_sum(c[1], asl);
+          v.z = f4::slice_sum(c[2], asl);
+          v.w = f4::slice_sum(c[3], asl);
           if constexpr (SPLIT) {
             if (writer) *reinterpret_cast<float4*>(pout) = v;
           } else {

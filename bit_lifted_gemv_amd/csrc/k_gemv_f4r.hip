@@ -4,10 +4,10 @@
 // (LiftQuant notes, 关键设计 4: after the activation transform the layer is a
 // product of 1-bit weights with floats, scaled per row by s).
 //
-// Matrix cores: sign bits as float4 (A) masked in place, each activation as
-// three float8 parts in B columns 3 b + p with a power-of-two hardware scale
-// per 1024-position slice; a slice's contribution is 2 R - sum a, with R the
-// sum of the activations whose bit is set (see expand).
+// Matrix-core operands as in f4_parts.h: sign bits as float4 (A) masked in
+// place, each activation as three float8 parts in B columns 3 b + p with a
+// power-of-two hardware scale per 1024-position slice; a slice contributes
+// 2 R - sum a, with R the sum of the activations whose bit is set.
 //
 // Work split.  Each workgroup owns a contiguous run of 16-row tiles and all
 // of K, so no partial sum leaves it and the call is one launch.  It applies
@@ -24,6 +24,7 @@
 // in order, scales by s and writes the row.  Deterministic.
 #include <type_traits>
 
+#include "f4_parts.h"
 #include "lq_internal.h"
 
 namespace lq {
@@ -39,8 +40,9 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+using f4::f32x4;
+using f4::i32x8;
+using f4::part_bytes;
 
 constexpr int kSliceBits = 1024;
 constexpr int kSliceBytes = kSliceBits / 8;     // 128 bytes of a row per slice
@@ -53,78 +55,8 @@ constexpr int kDepth = 4;                       // granules of weights in flight
 constexpr int kXFloats = 80;                    // activation registers per lane
 constexpr size_t kLdsBytes = 160 * 1024;
 
-// A operand of one 128-position step from a word of sign bits, with no bit
-// moved across nibbles: nibble t of dword q holds bit 4 t + q of w where it
-// stands, which as float4 (E2M1) is 0 or c_q = 0.5, 1, 2 for q = 0, 1, 2;
-// for q = 3 the bit moves one place down, 0 or c_3 = 2.  The B operand
-// carries a / c_q, so the step yields sum_k bit_k a_k, and with
-// sigma = 2 bit - 1 a slice's sum is 2 R - sum_k a_k.
-__device__ __forceinline__ i32x8 expand(uint32_t w) {
-  i32x8 a;
-  a[0] = static_cast<int>(w & 0x11111111u);
-  a[1] = static_cast<int>(w & 0x22222222u);
-  a[2] = static_cast<int>(w & 0x44444444u);
-  a[3] = static_cast<int>((w >> 1) & 0x44444444u);
-  a[4] = a[5] = a[6] = a[7] = 0;
-  return a;
-}
-
-__device__ __forceinline__ f32x4 mfma(const i32x8& a, const i32x8& b, const f32x4& c, int sc) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, 127, 0, sc);
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_from(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
-}
-
-constexpr int part_bytes(int nb) { return kSteps * 3 * nb * 4 * 32; }   // per slice
 // A wave converts whole slices (16 positions per lane): at most this many.
 constexpr int xs_per_wave(int nb) { return kXFloats / (16 * nb) > 0 ? kXFloats / (16 * nb) : 1; }
-
-// Largest of v over the wave (every lane gets it, in a scalar register).
-__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0xB1, 0xF, 0xF, false)));
-  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x4E, 0xF, 0xF, false)));
-  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x141, 0xF, 0xF, false)));
-  v = max(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x140, 0xF, 0xF, false)));
-  const uint32_t a = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 0));
-  const uint32_t b = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 16));
-  const uint32_t c = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 32));
-  const uint32_t d = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 48));
-  return max(max(a, b), max(c, d));
-}
-
-// Sum of v over the wave in a fixed order (every lane gets it).
-__device__ __forceinline__ float wave_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
-  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
-  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
-  return (a + b) + (c + d);
-}
-
-// Three float8 parts of four activations (already scaled by 2^e) packed in
-// byte order: d[p] byte j holds part p of y[j].
-__device__ __forceinline__ void split3(float y0a, float y0b, float y0c, float y0d, int d[3]) {
-  float y[4] = {y0a, y0b, y0c, y0d};
-#pragma unroll
-  for (int p = 0; p < 3; ++p) {
-    int q = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-    q = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], q, true);
-    d[p] = q;
-    if (p < 2) {
-      y[0] = 16.f * (y[0] - __builtin_amdgcn_cvt_f32_fp8(q, 0));
-      y[1] = 16.f * (y[1] - __builtin_amdgcn_cvt_f32_fp8(q, 1));
-      y[2] = 16.f * (y[2] - __builtin_amdgcn_cvt_f32_fp8(q, 2));
-      y[3] = 16.f * (y[3] - __builtin_amdgcn_cvt_f32_fp8(q, 3));
-    }
-  }
-}
 
 struct PlanR {
   int G;        // workgroups
@@ -198,26 +130,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_f4r_kernel(
   float sums[XS][NB];
 #pragma unroll
   for (int i = 0; i < XS; ++i) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      uint32_t mb = 0;
-      if (wave + kWaves * i < S) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          mb = max(mb, __float_as_uint(xv[i][b][c].x) & 0x7FFFFFFFu);
-          mb = max(mb, __float_as_uint(xv[i][b][c].y) & 0x7FFFFFFFu);
-          mb = max(mb, __float_as_uint(xv[i][b][c].z) & 0x7FFFFFFFu);
-          mb = max(mb, __float_as_uint(xv[i][b][c].w) & 0x7FFFFFFFu);
-        }
-        mb = wave_max(mb);
-        float sm = 0.f;
-#pragma unroll
-        for (int c = 0; c < 4; ++c)
-          sm += (xv[i][b][c].x + xv[i][b][c].y) + (xv[i][b][c].z + xv[i][b][c].w);
-        sums[i][b] = wave_sum(sm);
-      }
-      mbs[i][b] = mb;
-    }
+    if (wave + kWaves * i < S) f4::slice_stats<NB>(xv[i], mbs[i], sums[i]);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -247,44 +160,21 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_f4r_kernel(
   };
   static_for<kDepth>([&](auto ec) __attribute__((always_inline)) { issue(decltype(ec)::value); });
 
-  // 4. Parts of the slices into LDS: 2^e puts the slice's largest |x| in
-  // [64, 128) (its biased exponent f gives e = 133 - f), at most 2^118 so
-  // that every column scale stays a finite power of two; positions with
-  // q = position mod 4 are further scaled by 1 / c_q = 2, 1, 1/2, 1/2 (at
-  // most 256, inside float8's range).  Per part and per q a lane writes the
-  // dword of its positions q, q + 4, q + 8, q + 12 (consecutive slots of one
-  // B lane).
-  {
-    const int xw = lane >> 1, xh = lane & 1;    // word of the slice, half of it
-    const int xu = xw < 16 ? (xw & 3) : 4 + ((xw - 16) & 3);
-    const int xG = xw < 16 ? (xw >> 2) : ((xw - 16) >> 2);
+  // 4. Parts of the slices into LDS (f4::slice_parts).
 #pragma unroll
-    for (int i = 0; i < XS; ++i) {
-      const int t = wave + kWaves * i;
-      if (t < S) {
+  for (int i = 0; i < XS; ++i) {
+    const int t = wave + kWaves * i;
+    if (t < S) {
+      int e[NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-          const uint32_t mb = mbs[i][b];
-          const int e = mb == 0 ? 0 : min(133 - static_cast<int>(mb >> 23), 118);
-          if (lane == 0) {
-            esc[t * NB + b] = e;
-            asum[t * NB + b] = sums[i][b];
-          }
-          uint8_t* dst = parts + t * PB + (3 * b) * 128;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int kap = 32 * xG + 8 * q + 4 * xh;
-            const int off = (xu * NCOL * 4 + ((kap & 63) >> 4)) * 32 + (kap & 15) + (kap >= 64 ? 16 : 0);
-            const int eq = e + (q == 0 ? 1 : q == 1 ? 0 : -1);
-            int d[3];
-            split3(ldexpf(xv[i][b][0][q], eq), ldexpf(xv[i][b][1][q], eq),
-                   ldexpf(xv[i][b][2][q], eq), ldexpf(xv[i][b][3][q], eq), d);
-            *reinterpret_cast<int*>(dst + off) = d[0];
-            *reinterpret_cast<int*>(dst + off + 128) = d[1];
-            *reinterpret_cast<int*>(dst + off + 256) = d[2];
-          }
+      for (int b = 0; b < NB; ++b) {
+        e[b] = f4::slice_exponent(mbs[i][b]);
+        if (lane == 0) {
+          esc[t * NB + b] = e[b];
+          asum[t * NB + b] = sums[i][b];
         }
       }
+      f4::slice_parts<NB>(xv[i], e, parts + t * PB, lane);
     }
   }
   __syncthreads();
@@ -325,16 +215,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_f4r_kernel(
       f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0;
 #pragma unroll
       for (int u = 0; u < kSteps; u += 2) {
-        c0 = mfma(expand(wd[u]), bv[u], c0, scl);
-        c1 = mfma(expand(wd[u + 1]), bv[u + 1], c1, scl);
+        c0 = f4::mfma(f4::expand(wd[u]), bv[u], c0, scl);
+        c1 = f4::mfma(f4::expand(wd[u + 1]), bv[u + 1], c1, scl);
       }
-      // columns 3 b + p summed over the parts p; the slice's sum is 2 R - sum a
       const f32x4 c = c0 + c1;
       float4 v;
-      v.x = fmaf(2.f, c[0] + dpp_from<0x101>(c[0]) + dpp_from<0x102>(c[0]), -asl);
-      v.y = fmaf(2.f, c[1] + dpp_from<0x101>(c[1]) + dpp_from<0x102>(c[1]), -asl);
-      v.z = fmaf(2.f, c[2] + dpp_from<0x101>(c[2]) + dpp_from<0x102>(c[2]), -asl);
-      v.w = fmaf(2.f, c[3] + dpp_from<0x101>(c[3]) + dpp_from<0x102>(c[3]), -asl);
+      v.x = f4::slice_sum(c[0], asl);
+      v.y = f4::slice_sum(c[1], asl);
+      v.z = f4::slice_sum(c[2], asl);
+      v.w = f4::slice_sum(c[3], asl);
       if (bcol && cp == 0)
         *reinterpret_cast<float4*>(psum + ((static_cast<size_t>(rtl) * S + sl) * NB + cb) * kRows +
                                    4 * G) = v;

@@ -126,8 +126,6 @@ size_t gemv1_workspace_bytes(int64_t m, int64_t K);
 hipError_t launch_layer_b1(const void* a, lq_dtype dt, const void* t_inv, const float* M, int d,
                            int D, const uint32_t* w, int64_t m, int64_t K, int64_t ldw,
                            const float* s, float* out, void* ws, hipStream_t st);
-hipError_t launch_gemv1(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
-                        const float* a_lift, float* out, void* ws, hipStream_t st);
 
 // Few-token GEMV on the matrix cores (k_gemv_mfma.hip), 1 <= B <= 16.
 size_t gemv_mfma_workspace_bytes(int64_t m, int64_t K, int64_t B);
