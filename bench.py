@@ -77,14 +77,20 @@ def layer_bytes(m, n, d, D, B):
     return 2 * n * B + 2 * n * 128 + 4 * d * D + m * K // 8 + 4 * m + 4 * m * B
 
 
-def src_sha(name):
-    path = os.path.join(ROOT, "bit_lifted_gemv_amd", "csrc", name)
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+def src_sha(names):
+    """First 16 hex digits of sha256 over the named csrc files, in order."""
+    h = hashlib.sha256()
+    for name in ([names] if isinstance(names, str) else names):
+        h.update(open(os.path.join(ROOT, "bit_lifted_gemv_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+GEMV_SRC = ["f4_parts.h", "k_gemv_f4r.hip", "k_gemv_f4.hip"]
 
 
 def load_traffic(kernel_src, key):
     """HBM bytes per launch from a committed counter summary, if it was taken
-    on the current kernel source (else None)."""
+    on the current kernel source (a file or a list of files; else None)."""
     path = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(path):
         return None
@@ -228,13 +234,14 @@ def run_gpu(args):
     gemv_ms = sum(per.values()) / len(per)
     gemv_bytes_avg = sum(g_bytes) / len(g_bytes)
     achieved = gemv_bytes_avg / (gemv_ms * 1e-3) / 1e9
-    traffic = load_traffic("k_gemv1.hip", "layer_b1_lq19_8_70b" if fused else
-                           "gemv_lq19_8_70b_b1")
+    traffic = load_traffic("k_gemv1.hip" if fused else GEMV_SRC,
+                           "layer_b1_lq19_8_70b" if fused else "gemv_lq19_8_70b_b1")
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": ("lq_layer_b1 (gemv1_kernel with the lift in its table prologue + "
                            "gemv1_reduce_kernel)" if fused else
-                           "lq_gemv B=1 (gemv1_kernel + gemv1_reduce_kernel)"),
+                           "lq_gemv B=1: gemv_f4r_kernel (one launch) on 28672x8192, "
+                           "gemv_f4_kernel + gemv_f4_reduce_kernel on 8192x28672"),
                 "bytes_per_launch": int(gemv_bytes_avg),
                 "avg_launch_us": round(gemv_ms * 1e3, 3),
                 "per_shape_us": {f"{L.m}x{L.n}": round(per[j] * 1e3, 3)
@@ -682,12 +689,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16-tables+f32",
-        "precision": ("one token: float16 sums of 8 signed activations (each table scaled "
-                      "by an exact power of two), float32 accumulation; 2-5 tokens: three "
-                      "float8 parts per activation x float4 +-1 signs, float32 "
-                      "accumulation; 6-16 tokens: bfloat16 hi + lo parts; batch 512: "
-                      "16-bit operands, float32 accumulation"),
+        "dtype": "f8x3-parts+f32",
+        "precision": ("1-5 tokens: three float8 (E4M3) parts per lifted activation "
+                      "(12 significant bits, power-of-two scale per 1024-position slice) x "
+                      "float4 0/1 sign nibbles on the matrix cores, float32 accumulation, "
+                      "2R - sum(a) per slice in float32; 6-16 tokens: bfloat16 hi + lo "
+                      "parts; batch 512: 16-bit operands, float32 accumulation"),
         "data": "synthetic (seeded; shapes of the 70B-class LQ-19/8 MLP)",
         "config": {"workload": "LQ-19/8 70B-class MLP at batch 1: up 28672x8192 then down "
                                "8192x28672, lift + GEMV each, inputs bf16, weights 2.375 bit",

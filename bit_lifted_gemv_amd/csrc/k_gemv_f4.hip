@@ -258,58 +258,47 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_f4_kernel(
   }
 }
 
-// out[b][i] = s[i] * (sum over slices q of partials[i / 16][q][b][i % 16]),
-// in slice order: P lanes share a (row, token), lane part j adds slices j,
-// j + P, ... (at most 8 each, all loads in flight), then a fixed tree.
-template <int P>
+// out[b][i] = s[i] * (sum over slices q of partials[i / 16][q][b][i % 16]):
+// a wave per (16-row tile, token); lane (row l % 16, part l / 16) adds slices
+// part, part + 4, ... in order (every load four whole 64-byte runs of the
+// tile, all in flight), then the four parts are added in a fixed order.
 __global__ void __launch_bounds__(256) gemv_f4_reduce_kernel(const float* __restrict__ partials,
                                                              const float* __restrict__ s,
                                                              float* __restrict__ out, int64_t m,
-                                                             int S, int NB) {
-  constexpr int R = 64 / P;
+                                                             int S, int NB, int64_t units) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
-  const int part = lane % P;
-  const int64_t idx = wave * R + lane / P;      // (token, row) = (idx / m, idx % m)
-  const int64_t b = idx / m;
-  const int64_t row = idx - b * m;
+  const int64_t unit = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;   // g * NB + b
+  if (unit >= units) return;                    // whole waves
+  const int64_t g = unit / NB;
+  const int b = static_cast<int>(unit - g * NB);
+  const int r = lane & 15, part = lane >> 4;
+  const float* p = partials + ((g * S + part) * NB + b) * kGranuleRows + r;
+  const int64_t qstep = 4 * (int64_t)NB * kGranuleRows;
   float sum = 0.f;
-  if (b < NB) {
-    const float* p = partials + ((row >> 4) * S * NB + b) * kGranuleRows + (row & 15);
-    const int64_t qstep = (int64_t)NB * kGranuleRows;
-    for (int q0 = part; q0 < S; q0 += 8 * P) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int q = q0 + u * P;
-        v[u] = q < S ? p[(int64_t)q * qstep] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) sum += v[u];
-    }
+  int q = part;
+  for (; q + 12 < S; q += 16) {
+    const float v0 = p[0], v1 = p[qstep], v2 = p[2 * qstep], v3 = p[3 * qstep];
+    sum += v0;
+    sum += v1;
+    sum += v2;
+    sum += v3;
+    p += 4 * qstep;
   }
-#pragma unroll
-  for (int o = 1; o < P; o <<= 1) sum += __shfl_xor(sum, o);
-  if (b < NB && part == 0) out[b * m + row] = s[row] * sum;
-}
-
-template <int P>
-void launch_reduce(const float* partials, const float* s, float* out, int64_t m, int S, int NB,
-                   hipStream_t st) {
-  constexpr int per_block = 4 * (64 / P);
-  const int64_t n = m * NB;
-  hipLaunchKernelGGL(gemv_f4_reduce_kernel<P>, dim3(static_cast<unsigned>((n + per_block - 1) / per_block)),
-                     dim3(256), 0, st, partials, s, out, m, S, NB);
+  for (; q < S; q += 4) {
+    sum += p[0];
+    p += qstep;
+  }
+  sum += __shfl_xor(sum, 16);                   // parts 0 + 1, 2 + 3
+  sum += __shfl_xor(sum, 32);                   // (0 + 1) + (2 + 3)
+  const int64_t row = g * kGranuleRows + r;
+  if (part == 0 && row < m) out[b * m + row] = s[row] * sum;
 }
 
 void reduce_slices(const float* partials, const float* s, float* out, int64_t m, int S, int NB,
                    hipStream_t st) {
-  const int need = (S + 7) / 8;
-  if (need <= 1) launch_reduce<1>(partials, s, out, m, S, NB, st);
-  else if (need <= 2) launch_reduce<2>(partials, s, out, m, S, NB, st);
-  else if (need <= 4) launch_reduce<4>(partials, s, out, m, S, NB, st);
-  else if (need <= 8) launch_reduce<8>(partials, s, out, m, S, NB, st);
-  else launch_reduce<16>(partials, s, out, m, S, NB, st);
+  const int64_t units = (m + kGranuleRows - 1) / kGranuleRows * NB;
+  hipLaunchKernelGGL(gemv_f4_reduce_kernel, dim3(static_cast<unsigned>((units + 3) / 4)), dim3(256),
+                     0, st, partials, s, out, m, S, NB, units);
 }
 
 Sched make_sched(int64_t m, int64_t K) {
