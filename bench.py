@@ -693,8 +693,9 @@ def main():
         "precision": ("1-5 tokens: three float8 (E4M3) parts per lifted activation "
                       "(12 significant bits, power-of-two scale per 1024-position slice) x "
                       "float4 0/1 sign nibbles on the matrix cores, float32 accumulation, "
-                      "2R - sum(a) per slice in float32; 6-16 tokens: bfloat16 hi + lo "
-                      "parts; batch 512: 16-bit operands, float32 accumulation"),
+                      "2R - sum(a) per slice in float32; 6-16 tokens: the same parts "
+                      "(scale per 128-position step) as column blocks x float4 +-1 signs; "
+                      "batch 512: 16-bit operands, float32 accumulation"),
         "data": "synthetic (seeded; shapes of the 70B-class LQ-19/8 MLP)",
         "config": {"workload": "LQ-19/8 70B-class MLP at batch 1: up 28672x8192 then down "
                                "8192x28672, lift + GEMV each, inputs bf16, weights 2.375 bit",

@@ -44,18 +44,19 @@ constexpr int64_t kGemmMaxK = int64_t{1} << 22;
 // lq_gemv kernels: one to five tokens in one launch on the float4-sign /
 // float8-part matrix cores when a workgroup's LDS holds its sums (no
 // workspace), otherwise on the slice-major float8-part kernel and its slice
-// reduction; six to sixteen on the bfloat16 matrix cores.  (The float16
-// activation-sum table kernel serves lq_layer_b1.)
-enum class GemvPath { kRows, kF4, kBf16 };
+// reduction; six to sixteen on the float8-part kernel with the parts as
+// column blocks (preparation, product over splits of K, reduction).  (The
+// float16 activation-sum table kernel serves lq_layer_b1.)
+enum class GemvPath { kRows, kF4, kF4m };
 GemvPath gemv_path(int64_t m, int64_t K, int64_t B) {
   if (lq::gemv_f4r_applies(m, K, B)) return GemvPath::kRows;
-  return B <= 5 ? GemvPath::kF4 : GemvPath::kBf16;
+  return B <= 5 ? GemvPath::kF4 : GemvPath::kF4m;
 }
 size_t gemv_workspace(int64_t m, int64_t K, int64_t B) {
   switch (gemv_path(m, K, B)) {
     case GemvPath::kRows: return 0;
     case GemvPath::kF4: return lq::gemv_f4_workspace_bytes(m, K, B);
-    default: return lq::gemv_mfma_workspace_bytes(m, K, B);
+    default: return lq::gemv_f4m_workspace_bytes(m, K, B);
   }
 }
 
@@ -90,7 +91,7 @@ lq_status gemv_launch(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ld
       return hip_status(lq::launch_gemv_f4(w_packed, m, K, ldw, s, a_lift, B, out, ws, st),
                         "lq_gemv launch");
     default:
-      return hip_status(lq::launch_gemv_mfma(w_packed, m, K, ldw, s, a_lift, B, out, ws, st),
+      return hip_status(lq::launch_gemv_f4m(w_packed, m, K, ldw, s, a_lift, B, out, ws, st),
                         "lq_gemv launch");
   }
 }

@@ -127,10 +127,11 @@ hipError_t launch_layer_b1(const void* a, lq_dtype dt, const void* t_inv, const 
                            int D, const uint32_t* w, int64_t m, int64_t K, int64_t ldw,
                            const float* s, float* out, void* ws, hipStream_t st);
 
-// Few-token GEMV on the matrix cores (k_gemv_mfma.hip), 1 <= B <= 16.
-size_t gemv_mfma_workspace_bytes(int64_t m, int64_t K, int64_t B);
-hipError_t launch_gemv_mfma(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
-                            const float* a_lift, int64_t B, float* out, void* ws, hipStream_t st);
+// GEMV for 6 <= B <= 16 on float4 sign / float8 activation-part matrix
+// cores, the three parts as column blocks (k_gemv_f4m.hip).
+size_t gemv_f4m_workspace_bytes(int64_t m, int64_t K, int64_t B);
+hipError_t launch_gemv_f4m(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
+                           const float* a_lift, int64_t B, float* out, void* ws, hipStream_t st);
 
 // Few-token GEMV on float4 sign / float8 activation-part matrix cores
 // (k_gemv_f4.hip), 1 <= B <= 5.

@@ -263,13 +263,15 @@ lq_status lq_workspace_clear(void* workspace, size_t bytes, void* stream);
  * larger matrices by rows over several calls) and K <= 2^24.  Accumulation
  * is float32 and the result does not depend on timing (partial sums over the
  * lifted dimension are added in a fixed order, no float atomics).
- * Arithmetic: with B == 1 the kernel keeps tables of activation sums (not
- * of weights) in float16, each slice's activations scaled by an exact power
- * of two first, so every table entry carries one float16 rounding (relative
- * 2^-11) whatever the range of a_lift: a relative output error of about
- * 3e-4.  With B >= 2 the product runs on the matrix cores: each activation
- * is split into two bfloat16 parts (hi + lo, relative error below 2^-17)
- * and multiplied by exact +-1 signs.
+ * Arithmetic: the product runs on the matrix cores with the signs as
+ * float4 values (exact) and each activation carried by three float8 (E4M3)
+ * parts of 4 significant bits each, kept in range by a power-of-two scale
+ * per block of positions (1024 positions for B <= 5, 128 for B >= 6): 12
+ * significant bits per value (relative error at most 2^-12 of the value,
+ * less than 2^-17 of the block's largest one for small values), exact
+ * products, float32 sums; about 2e-5 relative output error on the workload
+ * shapes.  For B <= 5 the signs enter as 0 / c nibbles and each block adds
+ * 2 R - sum(a) (R: the sum over set bits, the block's sum taken in float32).
  */
 lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw,
                   const float* s, const float* a_lift, int64_t B, float* out,

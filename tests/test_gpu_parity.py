@@ -21,11 +21,12 @@ from oracle import lq_oracle as O
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
-# With B >= 2 the GEMV splits each float32 activation into two bfloat16 parts
-# (hi + lo carry 16 significant bits: relative error <= 2^-17 per value,
-# independent across the K values of a row) and multiplies them by exact +-1
-# on the matrix cores with float32 accumulation (about K/32 roundings of the
-# running sum): 1e-4 bounds both with a wide margin at every K here.
+# The GEMV carries each float32 activation by three float8 parts (12
+# significant bits, a relative error of at most 2^-12 per value, independent
+# across the K values of a row) and multiplies them by exact float4 signs on
+# the matrix cores with float32 accumulation (about K/128 roundings of the
+# running sum); the GEMM takes exact 16-bit operands: 1e-4 bounds both with
+# a wide margin at every K here.
 TOL_F32 = 1e-4
 # lq_layer_b1 rounds each activation sum (8 terms) once to float16 after an
 # exact power-of-two scaling: relative error <= 2^-11 per table entry,
@@ -232,6 +233,42 @@ def test_gemv_few_tokens_float8_parts(dev, m, K, B):
     per-slice column scales keep every part normal)."""
     _banner(f"gemv f4 m={m} K={K} B={B}")
     rng = np.random.default_rng(m * 13 + K + B)
+    ldw = ((K + 31) // 32 + 3) // 4 * 4
+    packed = synth.random_sign_words(rng, m, K, ldw=ldw)
+    al = rng.standard_normal((B, K)).astype(np.float32)
+    al[:, rng.choice(K, size=max(1, K // 100), replace=False)] *= 20
+    if K > 3 * 1024:
+        al[0, 1024:2048] = 0
+        al[-1, 2048:3072] *= np.float32(1e-30)
+        al[0, 3072:4096] *= np.float32(1e25)
+    s = rng.uniform(0.01, 0.03, m).astype(np.float32)
+    got = lq.gemv(torch.from_numpy(packed.view(np.int32)).to(dev), torch.from_numpy(s).to(dev),
+                  torch.from_numpy(al).to(dev), K).cpu().numpy()
+    ref = O.lifted_product(packed, K, al, s)
+    e = O.rel_err_colmax(got, ref)
+    _banner(f"  rel err {e:.3e}")
+    assert np.isfinite(got).all()
+    assert e <= TOL_F32, e
+
+
+F4M_CASES = [  # (m, K, B): 6..16 tokens, the float8 parts as column blocks
+    (1, 4, 6),          # one row, one word
+    (65, 516, 16),      # a ragged tile and a 4-position last word
+    (513, 20480, 11),   # one row past a workgroup's 512
+    (520, 9216, 7),
+    (8192, 2048, 16),   # many row groups, one span pair per split
+    (64, 300000, 9),    # one row group: as many splits as span pairs allow
+    (4096, 28672, 16),
+]
+
+
+@pytest.mark.parametrize("m,K,B", F4M_CASES)
+def test_gemv_many_tokens_float8_parts(dev, m, K, B):
+    """6 <= B <= 16 with the float8 parts as column blocks, with outlier
+    channels (1 % x 20), a run of zeros, and runs of tiny and huge activations
+    (the per-step exponents keep every part normal)."""
+    _banner(f"gemv f4m m={m} K={K} B={B}")
+    rng = np.random.default_rng(m * 17 + K + B)
     ldw = ((K + 31) // 32 + 3) // 4 * 4
     packed = synth.random_sign_words(rng, m, K, ldw=ldw)
     al = rng.standard_normal((B, K)).astype(np.float32)
