@@ -61,7 +61,7 @@ constexpr int kSpanWords = 16;
 constexpr int kPartBytes = 4 * 3 * 64 * 32;            // per span
 constexpr int kSpanBytes = kPartBytes + 4 * 16 * 4;    // parts, then exponents
 constexpr int kSpanVec = kSpanBytes / 16;
-constexpr int kRT = 4;                                 // 16-row tiles per wave
+constexpr int kRT = 2;                                 // 16-row tiles per wave
 
 // A per-lane value the compiler cannot fold (kept in a vector register).
 __device__ __forceinline__ uint32_t opaque_v(uint32_t v) {
