@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--gemm-dtype", default="f16", choices=["f16", "bf16"])
     p.add_argument("--no-cases", action="store_true", help="skip the per-workload sweep")
+    p.add_argument("--tokens", type=int, default=0,
+                   help="cases: only the workload cases with this many tokens")
     p.add_argument("--layer-path", default="split", choices=["fused", "split"],
                    help="one-token step: the lift inside the GEMV (lq_layer_b1) or the lift "
                         "and the GEMV as two calls")
@@ -139,7 +141,7 @@ def run_gpu(args):
     if args.only == "gemm":
         return dict(gemm=run_gemm(args, torch, lq, synth, dev))
     if args.only == "cases":
-        return dict(cases=run_cases(torch, lq, synth, dev))
+        return dict(cases=run_cases(torch, lq, synth, dev, args.tokens))
     if args.only == "kron":
         return dict(kron=run_kron(torch, lq, synth, dev))
     if args.only == "encode":
@@ -555,13 +557,13 @@ def run_kron(torch, lq, synth, dev):
     return res
 
 
-def run_cases(torch, lq, synth, dev):
+def run_cases(torch, lq, synth, dev, tokens=0):
     """GEMV (B <= 16) per workload case: graphs of back-to-back launches on
-    rotating copies."""
+    rotating copies (only the cases with `tokens` tokens when it is set)."""
     res = []
     st = torch.cuda.current_stream()
     for cfg, si, (m, n), B in synth.all_cases():
-        if B > 16:
+        if B > 16 or (tokens and B != tokens):
             continue
         L = synth.make_case(cfg, si, B)
         rot = Rotation(L, torch, lq, dev)
