@@ -125,6 +125,9 @@ KRON_CASES = [  # (n, n1, d, D, B, act dtype): n2 = n / n1 <= 128, n2 % d == 0
     (1280, 16, 10, 24, 1, "f16"), (512, 4, 8, 20, 3, "bf16"), (8192, 64, 16, 40, 1, "bf16"),
     (8192, 64, 16, 40, 17, "f16"), (28672, 224, 8, 19, 1, "bf16"), (4096, 32, 8, 20, 5, "f32"),
     (384, 3, 4, 9, 2, "bf16"), (960, 12, 8, 16, 7, "bf16"), (6, 2, 3, 5, 1, "f32"),
+    # 16 | n1 and 16 | n2 with d = 1, 2, 4 at a few tokens (n1 = 48: three
+    # 16-row blocks; n2 = 16: one column block)
+    (3072, 48, 4, 12, 2, "f16"), (2048, 16, 1, 3, 8, "bf16"), (1024, 64, 2, 5, 1, "f32"),
     # 64 tokens and more with small factors take the single-launch kernel:
     # the prefill-scale shape, a ragged last token group, D % 4 != 0, float32
     # activations, several tokens per workgroup
