@@ -34,16 +34,15 @@
 // 16 (g / 2) .. 16 (g / 2) + 15.
 //
 // Kernels.  A preparation kernel writes every word's parts and exponent
-// once to the workspace, in the order the B operand is read (per span:
-// [step][part][half][lane][16 bytes], so that each 16-byte LDS read of a
-// wave covers 1 KB of consecutive banks, then [step][token] exponents).  The main
-// kernel gives each wave RT tiles of 16 rows; the 8 waves of a workgroup
-// share the parts of one span at a time in LDS (double-buffered, loaded into
-// registers two spans ahead and written to LDS one span ahead) and stream
-// their weights two spans ahead in registers.  The lifted dimension is split
-// over S workgroups so that every compute unit holds one; each split writes
-// float32 partial sums to the workspace and a reduction kernel adds them in
-// split order and scales by s.  Deterministic.
+// once to the workspace, in the order a lane holds its B operand (per span:
+// [step][part][half][lane][16 bytes], then [step][token] exponents).  In the
+// main kernel each wave keeps one span's B operands in registers for the
+// whole kernel and streams its workgroup's row tiles through them; the
+// eight waves of a workgroup hold eight consecutive spans, and their partial
+// tiles are added in wave order through LDS.  The lifted dimension is split
+// into runs of eight spans, one per workgroup row; each split writes float32
+// partial sums to the workspace and a reduction kernel adds them in split
+// order and scales by s.  Deterministic.
 #include "lq_internal.h"
 
 #include <type_traits>
@@ -61,7 +60,6 @@ constexpr int kSpanWords = 16;
 constexpr int kPartBytes = 4 * 3 * 64 * 32;            // per span
 constexpr int kSpanBytes = kPartBytes + 4 * 16 * 4;    // parts, then exponents
 constexpr int kSpanVec = kSpanBytes / 16;
-constexpr int kRT = 2;                                 // 16-row tiles per wave
 
 // A per-lane value the compiler cannot fold (kept in a vector register).
 __device__ __forceinline__ uint32_t opaque_v(uint32_t v) {
@@ -168,142 +166,174 @@ __global__ void __launch_bounds__(256) gemv_f4m_prep_kernel(const float* __restr
   if (g == 0 && h == 0) reinterpret_cast<int*>(span + kPartBytes)[u * 16 + n] = e;
 }
 
-// RT: 16-row tiles per wave; kW: waves per workgroup.  Grid: x = row groups,
-// y = splits of the lifted dimension (whole span pairs each).
-template <int RT, int kW>
-__global__ void __launch_bounds__(64 * kW, 1) gemv_f4m_kernel(
+// Main kernel.  A workgroup of 8 waves owns TW tiles of 16 rows and eight
+// consecutive spans (4096 positions); wave w keeps the B operands of span
+// 8 y + w (four steps, three parts: 96 registers) for the whole kernel and
+// streams the workgroup's tiles through them, T tiles per batch, with the
+// weights of the next two batches in flight.  After each batch the eight
+// waves' partial tiles go to LDS and are added in wave order (one barrier
+// per batch, two LDS buffers) into an LDS stage of the workgroup's sums,
+// which is written out once at the end: the loop issues no global stores,
+// so its waits on the weight loads stay exact.  Grid: x = row groups of TW
+// tiles, y = splits of eight spans.
+template <int T>
+__global__ void __launch_bounds__(512, 1) gemv_f4m_kernel(
     const uint32_t* __restrict__ w, int m, int ldw, int nw, const uint8_t* __restrict__ bws,
-    int nspans, int B, float* __restrict__ partials) {
-  constexpr int kThreads = 64 * kW;
-  // parts: kPer vectors per thread; exponents: 16 vectors, threads 0 .. 15
-  constexpr int kPer = kPartBytes / 16 / kThreads;
-  static_assert(kPer * kThreads * 16 == kPartBytes, "whole vectors per thread");
-  __shared__ u32x4 sb[2][kSpanVec];
+    int TW, int B, float* __restrict__ partials) {
+  constexpr int kW = 8;
+  static_assert(T == 4, "the sums of a batch: one thread per (tile, lane, row pair)");
+  extern __shared__ f32x4 red[];                // [2][kW][T][64], then the stage [16][(TW + 2 T) 16]
+  float* stage = reinterpret_cast<float*>(red + 2 * kW * T * 64);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int i = lane & 15;
   const int g = lane >> 4;
-  // this split's spans: a whole number of span pairs (nspans is even)
-  const int S = gridDim.y;
-  const int c0 = 2 * (blockIdx.y * (nspans / 2) / S);
-  const int c1 = 2 * ((blockIdx.y + 1) * (nspans / 2) / S);
+  const int c = blockIdx.y * kW + wave;         // this wave's span
 
-  // Weights of this workgroup's rows: rows past m read as zero and are
-  // never stored; words past a row's last one, nw, are not fetched (they
-  // read as zero) and meet zero activations.
-  const int wg_row0 = blockIdx.x * kW * 16 * RT;
-  const int wg_rows = min(kW * 16 * RT, m - wg_row0);
-  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t*>(w + static_cast<int64_t>(wg_row0) * ldw), (short)0,
-      static_cast<int>(static_cast<uint32_t>(wg_rows) * static_cast<uint32_t>(ldw) * 4u), kRsrcWord3);
-  uint32_t w_off[RT];
+  // B operands of the span: [step][part] with both 16-byte halves, and the
+  // exponent of column i at each step.
+  i32x8 bq[4][3];
+  int ex[4];
+  {
+    const uint8_t* sp = bws + static_cast<int64_t>(c) * kSpanBytes;
 #pragma unroll
-  for (int t = 0; t < RT; ++t)
-    w_off[t] = static_cast<uint32_t>((wave * 16 * RT + t * 16 + i) * ldw + 4 * g) * 4u;
-  auto load_w = [&](int c, int t) -> uint4 {
-    const int word0 = c * kSpanWords + 4 * g;
-    const uint32_t vo = word0 < nw ? w_off[t] : kFar;
-    const int so = c < c1 ? c * kSpanWords * 4 : static_cast<int>(kFar);
-    const auto r = __builtin_amdgcn_raw_buffer_load_b128(wres, vo, so, 0);
-    uint4 v;
-    __builtin_memcpy(&v, &r, 16);
-    return v;
-  };
-  const u32x4* bsrc = reinterpret_cast<const u32x4*>(bws);
-  const int xe = tid < 16 ? tid : 0;            // exponent vector of this thread
-  auto load_b = [&](int c, u32x4 (&v)[kPer + 1]) {
-    const u32x4* src = bsrc + static_cast<int64_t>(c) * kSpanVec;
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) v[k] = src[tid + k * kThreads];
-    v[kPer] = src[kPer * kThreads + xe];
-  };
-  auto store_b = [&](int buf, const u32x4 (&v)[kPer + 1]) {
-#pragma unroll
-    for (int k = 0; k < kPer; ++k) sb[buf][tid + k * kThreads] = v[k];
-    if (tid < 16) sb[buf][kPer * kThreads + tid] = v[kPer];
-  };
-
-  f32x4 acc[RT];
-#pragma unroll
-  for (int t = 0; t < RT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint32_t two = opaque_v(0x22222222u);
-
-  uint4 wv[2][RT];
-  u32x4 nbv[2][kPer + 1];
-#pragma unroll
-  for (int t = 0; t < RT; ++t) wv[0][t] = load_w(c0, t);
-#pragma unroll
-  for (int t = 0; t < RT; ++t) wv[1][t] = load_w(c0 + 1, t);
-  load_b(c0, nbv[0]);
-  load_b(c0 + 1, nbv[1]);
-  store_b(0, nbv[0]);
-  __syncthreads();
-
-  // One span, c % 2 == P (counted from c0): wv[P] holds its weights, LDS
-  // buffer P its parts, nbv[P ^ 1] the next span's parts.  The parts of span
-  // c + 2 are loaded first (into nbv[P]); the weight registers are refilled
-  // with span c + 2 after the last step; the next span's parts go to the
-  // other buffer at the end.
-  auto span = [&](auto P, int c) {
-    constexpr int p = decltype(P)::value;
-    load_b(c + 2, nbv[p]);
-    const uint8_t* sp = reinterpret_cast<const uint8_t*>(&sb[p][0]);
-    const int* se = reinterpret_cast<const int*>(sp + kPartBytes);
-    // B operands of step u (three parts) and its exponent, read one step
-    // ahead of their products
-    auto read_step = [&](int u, i32x8 (&bf)[3], int& e) {
+    for (int u = 0; u < 4; ++u) {
 #pragma unroll
       for (int q = 0; q < 3; ++q) {
         const uint4 y0 = *reinterpret_cast<const uint4*>(sp + (((u * 3 + q) * 2) * 64 + lane) * 16);
         const uint4 y1 = *reinterpret_cast<const uint4*>(sp + (((u * 3 + q) * 2 + 1) * 64 + lane) * 16);
-        __builtin_memcpy(&bf[q], &y0, 16);
-        __builtin_memcpy(reinterpret_cast<char*>(&bf[q]) + 16, &y1, 16);
+        __builtin_memcpy(&bq[u][q], &y0, 16);
+        __builtin_memcpy(reinterpret_cast<char*>(&bq[u][q]) + 16, &y1, 16);
       }
-      e = se[u * 16 + i];
-    };
-    i32x8 bf[2][3];
-    int ex[2];
-    read_step(0, bf[0], ex[0]);
+      ex[u] = reinterpret_cast<const int*>(sp + kPartBytes)[u * 16 + i];
+    }
+  }
+
+  // Weights of this workgroup's rows: rows past its last read as zero and
+  // are never stored; words past a row's last one, nw, read as zero (they
+  // meet zero activations).
+  const int NT = (m + 15) / 16;
+  const int tile0 = blockIdx.x * TW;
+  const int nt = min(TW, NT - tile0);           // tiles of this workgroup (>= 1)
+  const int wg_row0 = tile0 * 16;
+  const int wg_rows = min(TW * 16, m - wg_row0);
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(w + static_cast<int64_t>(wg_row0) * ldw), (short)0,
+      static_cast<int>(static_cast<uint32_t>(wg_rows) * static_cast<uint32_t>(ldw) * 4u), kRsrcWord3);
+  const uint32_t w_lane = c * kSpanWords + 4 * g < nw
+      ? static_cast<uint32_t>(i * ldw + c * kSpanWords + 4 * g) * 4u : kFar;
+  const uint32_t tile_bytes = static_cast<uint32_t>(16 * ldw) * 4u;
+  auto load_w = [&](int j) -> uint4 {           // tile j of the workgroup
+    const int so = j < nt ? static_cast<int>(j * tile_bytes) : static_cast<int>(kFar);
+    const auto r = __builtin_amdgcn_raw_buffer_load_b128(wres, w_lane, so, 0);
+    uint4 v;
+    __builtin_memcpy(&v, &r, 16);
+    return v;
+  };
+
+  const uint32_t two = opaque_v(0x22222222u);
+  const int nb = (nt + T - 1) / T;              // batches
+  uint4 wv[2][T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) wv[0][t] = load_w(t);
+#pragma unroll
+  for (int t = 0; t < T; ++t) wv[1][t] = load_w(T + t);
+  // the span's operands are in registers before the loop (waited for here,
+  // behind the first weight loads, so that the loop's waits count only
+  // weight loads)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) asm volatile("" : "+v"(bq[u][q]));
+    asm volatile("" : "+v"(ex[u]));
+  }
+  const int st_t = (tid >> 6) & 3;              // tile of the batch
+  const int st_h = tid >> 8;                    // rows 2 h, 2 h + 1 of the lane's four
+  // The stage holds a batch of rows before the first (where the sums of
+  // the batch before batch 0 land) and one after the last (the second of a
+  // pair past nb), so its writes need no branch.
+  const int TR = (TW + 2 * T) * 16;             // stage row stride (per token)
+
+  // The sums of the batch whose partial tiles are in LDS buffer q, in wave
+  // order, into the stage rows of batch bb (acc[r] of (tile t, lane) is
+  // D[row 4 g + r][token i]).
+  auto batch_sums = [&](int q, int bb) {
+    const float2* rb2 = reinterpret_cast<const float2*>(red + q * kW * T * 64);
+    float2 y[kW];
+#pragma unroll
+    for (int k = 0; k < kW; ++k) y[k] = rb2[((k * T + st_t) * 64 + lane) * 2 + st_h];
+    float2 v = y[0];
+#pragma unroll
+    for (int k = 1; k < kW; ++k) {
+      v.x += y[k].x;
+      v.y += y[k].y;
+    }
+    const int r = ((bb + 1) * T + st_t) * 16 + 4 * g + 2 * st_h;
+    *reinterpret_cast<float2*>(stage + i * TR + r) = v;
+  };
+
+  // Batch b (b % 2 == P): the sums of batch b - 1 (LDS buffer P ^ 1) are
+  // formed while the batch's products run; then the weights are refilled
+  // with batch b + 2, the partial tiles go to LDS buffer P, one barrier.
+  auto batch = [&](auto P, int b) {
+    constexpr int p = decltype(P)::value;
+    // the batch's products stay after the previous batch's barrier (they
+    // need no memory, so the scheduler would otherwise hoist them and wait
+    // for both batches' weights at once)
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (u < 3) read_step(u + 1, bf[(u + 1) & 1], ex[(u + 1) & 1]);
-      // keeps the reads of later steps from being hoisted into registers
-      asm volatile("" ::: "memory");
 #pragma unroll
-      for (int t = 0; t < RT; ++t) {
+      for (int t = 0; t < T; ++t) {
         const uint32_t W = u == 0 ? wv[p][t].x : u == 1 ? wv[p][t].y : u == 2 ? wv[p][t].z : wv[p][t].w;
         const i32x8 a = expand_pm(W, two);
 #pragma unroll
-        for (int q = 0; q < 3; ++q) acc[t] = mfma(a, bf[u & 1][q], acc[t], 127 - ex[u & 1] - 4 * q);
+        for (int q = 0; q < 3; ++q) acc[t] = mfma(a, bq[u][q], acc[t], 127 - ex[u] - 4 * q);
       }
-      // the step's products are issued here, not sunk past later steps
-#pragma unroll
-      for (int t = 0; t < RT; ++t) asm volatile("" : "+v"(acc[t]));
+      if (u == 0) batch_sums(p ^ 1, b - 1);
     }
 #pragma unroll
-    for (int t = 0; t < RT; ++t) wv[p][t] = load_w(c + 2, t);
-    store_b(p ^ 1, nbv[p ^ 1]);
+    for (int t = 0; t < T; ++t) asm volatile("" : "+v"(acc[t]));
+#pragma unroll
+    for (int t = 0; t < T; ++t) wv[p][t] = load_w((b + 2) * T + t);
+    f32x4* rb = red + p * kW * T * 64;
+#pragma unroll
+    for (int t = 0; t < T; ++t) rb[(wave * T + t) * 64 + lane] = acc[t];
     __syncthreads();
   };
-  // Pairs of spans without branches inside the loop body, so the waits on
-  // the loads are the same every turn.  The workspace holds two spans more
-  // than the layer needs, for the part loads two spans ahead.
-  for (int c = c0; c < c1; c += 2) {
-    span(std::integral_constant<int, 0>{}, c);
-    span(std::integral_constant<int, 1>{}, c + 1);
-  }
+  // pairs of batches (nb >= 1), no branch before the first
+  int b = 0;
+  do {
+    batch(std::integral_constant<int, 0>{}, b);
+    batch(std::integral_constant<int, 1>{}, b + 1);
+    b += 2;
+  } while (b < nb);
+  batch_sums(1, b - 1);
+  __syncthreads();
 
-  // Epilogue.  acc[t][r] = D[row 4 g + r][token i] of tile t (-sum sigma a).
-  float* dst = partials + static_cast<int64_t>(blockIdx.y) * B * m;
-#pragma unroll
-  for (int t = 0; t < RT; ++t) {
-    const int row0 = wg_row0 + wave * 16 * RT + t * 16 + 4 * g;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = row0 + r;
-      if (row < m && i < B) dst[static_cast<int64_t>(i) * m + row] = acc[t][r];
+  // this split's partials [B][m], row-contiguous per token: 32 threads a
+  // token, four rows a thread (one 16-byte store when m % 4 == 0)
+  float* dst = partials + static_cast<int64_t>(blockIdx.y) * B * m + wg_row0;
+  const float* src = stage + T * 16;
+  const int n = tid >> 5;
+  if (n < B) {
+    for (int r = (tid & 31) * 4; r < wg_rows; r += 128) {
+      const float4 v = *reinterpret_cast<const float4*>(src + n * TR + r);
+      float* d = dst + static_cast<int64_t>(n) * m + r;
+      if ((m & 3) == 0 && r + 4 <= wg_rows) {
+        *reinterpret_cast<float4*>(d) = v;
+      } else {
+        d[0] = v.x;
+        if (r + 1 < wg_rows) d[1] = v.y;
+        if (r + 2 < wg_rows) d[2] = v.z;
+        if (r + 3 < wg_rows) d[3] = v.w;
+      }
     }
   }
 }
@@ -330,27 +360,34 @@ __global__ void __launch_bounds__(256) gemv_f4m_reduce_kernel(const float* __res
   out[idx] = -s[idx % m] * v;
 }
 
+constexpr int kT = 4;                                 // tiles per batch
+constexpr int kSpansWG = 8;                           // spans per workgroup (one per wave)
+constexpr int kMaxTW = 84;                            // tiles per workgroup: (84 + 8) KB of sums in LDS
+
 struct Plan {
-  int RT, W, S, nspans;
-  size_t b_bytes, p_bytes;
+  int S, TW, groups, nspans;                 // splits, tiles per workgroup, row groups, spans written
+  size_t b_bytes, p_bytes, lds;
 };
 
 Plan plan(int64_t m, int64_t K, int64_t B) {
   Plan p;
-  p.RT = kRT;
-  p.W = 8;                                   // waves per workgroup (2 per SIMD)
-  // an even number of spans (a padding span of zero activations adds nothing)
   const int64_t nwords = (K + 31) / 32;
-  p.nspans = static_cast<int>((nwords + 2 * kSpanWords - 1) / (2 * kSpanWords) * 2);
-  // as many splits of the lifted dimension as keep one workgroup per CU
-  const int64_t groups = (m + 16 * p.RT * p.W - 1) / (16 * p.RT * p.W);
-  int64_t S = num_cus() / groups;
-  S = S < 1 ? 1 : S;
-  S = S > p.nspans / 2 ? p.nspans / 2 : S;
-  p.S = static_cast<int>(S);
-  // the layer's spans plus two read ahead of the last (never used)
-  p.b_bytes = static_cast<size_t>(p.nspans + 2) * kSpanBytes;
+  const int64_t nsp = (nwords + kSpanWords - 1) / kSpanWords;
+  p.S = static_cast<int>((nsp + kSpansWG - 1) / kSpansWG);
+  // row groups: about one workgroup per CU, whole batches each, and each
+  // workgroup's sums within the LDS stage
+  const int64_t NT = (m + 15) / 16;
+  int64_t G = num_cus() / p.S;
+  G = G < 1 ? 1 : G;
+  int64_t TW = (NT + G - 1) / G;
+  TW = (TW + kT - 1) / kT * kT;
+  TW = TW > kMaxTW ? kMaxTW : TW;
+  p.TW = static_cast<int>(TW);
+  p.groups = static_cast<int>((NT + TW - 1) / TW);
+  p.nspans = p.S * kSpansWG;                 // padding spans are zero
+  p.b_bytes = static_cast<size_t>(p.nspans) * kSpanBytes;
   p.p_bytes = static_cast<size_t>(p.S) * B * m * 4;
+  p.lds = static_cast<size_t>(2) * 8 * kT * 64 * 16 + static_cast<size_t>(16) * (TW + 2 * kT) * 16 * 4;
   return p;
 }
 
@@ -366,14 +403,18 @@ hipError_t launch_gemv_f4m(const uint32_t* w, int64_t m, int64_t K, int64_t ldw,
   const Plan p = plan(m, K, B);
   uint8_t* bws = static_cast<uint8_t*>(ws);
   float* partials = reinterpret_cast<float*>(bws + p.b_bytes);
-  const int prep_threads = (p.nspans + 2) * 4 * 16 * 8;
+  const int prep_threads = p.nspans * 4 * 16 * 8;
   hipLaunchKernelGGL(gemv_f4m_prep_kernel, dim3((prep_threads + 255) / 256), dim3(256), 0, st,
-                     a_lift, static_cast<int>(B), static_cast<int>(K), p.nspans + 2, bws);
-  constexpr int RT = kRT, W = 8;
-  const int rows_wg = W * 16 * RT;
-  const dim3 grid(static_cast<unsigned>((m + rows_wg - 1) / rows_wg), static_cast<unsigned>(p.S));
-  hipLaunchKernelGGL((gemv_f4m_kernel<RT, W>), grid, dim3(64 * W), 0, st, w, static_cast<int>(m),
-                     static_cast<int>(ldw), static_cast<int>((K + 31) / 32), bws, p.nspans,
+                     a_lift, static_cast<int>(B), static_cast<int>(K), p.nspans, bws);
+  const void* fn = reinterpret_cast<const void*>(gemv_f4m_kernel<kT>);
+  if (p.lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(p.lds));
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid(static_cast<unsigned>(p.groups), static_cast<unsigned>(p.S));
+  hipLaunchKernelGGL((gemv_f4m_kernel<kT>), grid, dim3(512), p.lds, st, w, static_cast<int>(m),
+                     static_cast<int>(ldw), static_cast<int>((K + 31) / 32), bws, p.TW,
                      static_cast<int>(B), partials);
   const int64_t n = B * m;
   hipLaunchKernelGGL(gemv_f4m_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
