@@ -192,25 +192,6 @@ __global__ void __launch_bounds__(512, 1) gemv_f4m_kernel(
   const int g = lane >> 4;
   const int c = blockIdx.y * kW + wave;         // this wave's span
 
-  // B operands of the span: [step][part] with both 16-byte halves, and the
-  // exponent of column i at each step.
-  i32x8 bq[4][3];
-  int ex[4];
-  {
-    const uint8_t* sp = bws + static_cast<int64_t>(c) * kSpanBytes;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int q = 0; q < 3; ++q) {
-        const uint4 y0 = *reinterpret_cast<const uint4*>(sp + (((u * 3 + q) * 2) * 64 + lane) * 16);
-        const uint4 y1 = *reinterpret_cast<const uint4*>(sp + (((u * 3 + q) * 2 + 1) * 64 + lane) * 16);
-        __builtin_memcpy(&bq[u][q], &y0, 16);
-        __builtin_memcpy(reinterpret_cast<char*>(&bq[u][q]) + 16, &y1, 16);
-      }
-      ex[u] = reinterpret_cast<const int*>(sp + kPartBytes)[u * 16 + i];
-    }
-  }
-
   // Weights of this workgroup's rows: rows past its last read as zero and
   // are never stored; words past a row's last one, nw, read as zero (they
   // meet zero activations).
@@ -235,26 +216,44 @@ __global__ void __launch_bounds__(512, 1) gemv_f4m_kernel(
 
   const uint32_t two = opaque_v(0x22222222u);
   const int nb = (nt + T - 1) / T;              // batches
+  // the first batch's weights go out before the span's operands, so that
+  // batch 0 can start on each step's operands as they arrive
   uint4 wv[2][T];
 #pragma unroll
   for (int t = 0; t < T; ++t) wv[0][t] = load_w(t);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // B operands of the span: [step][part] with both 16-byte halves, and the
+  // exponent of column i at each step.
+  i32x8 bq[4][3];
+  int ex[4];
+  {
+    const uint8_t* sp = bws + static_cast<int64_t>(c) * kSpanBytes;
+    // exponents first, then the operands step by step (the order they are
+    // needed in)
 #pragma unroll
-  for (int t = 0; t < T; ++t) wv[1][t] = load_w(T + t);
-  // the span's operands are in registers before the loop (waited for here,
-  // behind the first weight loads, so that the loop's waits count only
-  // weight loads)
+    for (int u = 0; u < 4; ++u) ex[u] = reinterpret_cast<const int*>(sp + kPartBytes)[u * 16 + i];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int q = 0; q < 3; ++q) {
+        const uint4 y0 = *reinterpret_cast<const uint4*>(sp + (((u * 3 + q) * 2) * 64 + lane) * 16);
+        const uint4 y1 = *reinterpret_cast<const uint4*>(sp + (((u * 3 + q) * 2 + 1) * 64 + lane) * 16);
+        __builtin_memcpy(&bq[u][q], &y0, 16);
+        __builtin_memcpy(reinterpret_cast<char*>(&bq[u][q]) + 16, &y1, 16);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-#pragma unroll
-    for (int q = 0; q < 3; ++q) asm volatile("" : "+v"(bq[u][q]));
-    asm volatile("" : "+v"(ex[u]));
-  }
+  for (int t = 0; t < T; ++t) wv[1][t] = load_w(T + t);
   const int st_t = (tid >> 6) & 3;              // tile of the batch
   const int st_h = tid >> 8;                    // rows 2 h, 2 h + 1 of the lane's four
   // The stage holds a batch of rows before the first (where the sums of
-  // the batch before batch 0 land) and one after the last (the second of a
-  // pair past nb), so its writes need no branch.
+  // the batch before batch 0 land) and one after the last, so its writes
+  // need no branch.
   const int TR = (TW + 2 * T) * 16;             // stage row stride (per token)
 
   // The sums of the batch whose partial tiles are in LDS buffer q, in wave
@@ -307,14 +306,36 @@ __global__ void __launch_bounds__(512, 1) gemv_f4m_kernel(
     for (int t = 0; t < T; ++t) rb[(wave * T + t) * 64 + lane] = acc[t];
     __syncthreads();
   };
-  // pairs of batches (nb >= 1), no branch before the first
-  int b = 0;
-  do {
-    batch(std::integral_constant<int, 0>{}, b);
-    batch(std::integral_constant<int, 1>{}, b + 1);
-    b += 2;
-  } while (b < nb);
-  batch_sums(1, b - 1);
+  // Batch 0 on its own: its products wait for the span's operands step by
+  // step as they arrive.  Then the operands are marked as in registers, so
+  // that the loops' waits count only weight loads.  With nb even, batch 1
+  // is taken on its own too; the rest go in pairs (buffers alternate, so a
+  // loop body holds one batch of each parity).
+  batch(std::integral_constant<int, 0>{}, 0);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+#pragma unroll
+    for (int q = 0; q < 3; ++q) asm volatile("" : "+v"(bq[u][q]));
+    asm volatile("" : "+v"(ex[u]));
+  }
+  if (nb & 1) {
+    int b = 1;
+    while (b < nb) {
+      batch(std::integral_constant<int, 1>{}, b);
+      batch(std::integral_constant<int, 0>{}, b + 1);
+      b += 2;
+    }
+    batch_sums(0, nb - 1);
+  } else {
+    batch(std::integral_constant<int, 1>{}, 1);
+    int b = 2;
+    while (b < nb) {
+      batch(std::integral_constant<int, 0>{}, b);
+      batch(std::integral_constant<int, 1>{}, b + 1);
+      b += 2;
+    }
+    batch_sums(1, nb - 1);
+  }
   __syncthreads();
 
   // this split's partials [B][m], row-contiguous per token: 32 threads a
