@@ -292,7 +292,7 @@ def test_gemv_many_tokens_float8_parts(dev, m, K, B):
 
 ROWS_CASES = [  # (m, K, B) on the one-launch kernel (every slice in one workgroup's LDS)
     (1, 4, 1),          # one row, one 4-position slice
-    (4100, 40960, 1),   # 40 slices, the most one token takes; a last workgroup of one row tile
+    (4100, 20480, 1),   # 20 slices, the most one token takes; a last workgroup of one row tile
     (4097, 3072, 1),    # a ragged last row tile of one row
     (300, 16384, 2),    # 16 slices, the most two tokens take
     (33, 7200, 3),      # a ragged last slice
