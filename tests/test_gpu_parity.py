@@ -290,6 +290,36 @@ def test_gemv_many_tokens_float8_parts(dev, m, K, B):
     assert e <= TOL_F32, e
 
 
+F4M_LOOP_CASES = [  # (m, K, B): batches of four row tiles per workgroup
+    (36864, 4096, 11),    # one split, 12 tiles per workgroup: 3 batches (odd)
+    (65536, 4096, 16),    # one split, 16 tiles per workgroup: 4 batches (even)
+    (8192, 65536, 16),    # 16 splits, 32 tiles per workgroup: 8 batches
+    (12288, 131072, 6),   # 32 splits, the cap of 84 tiles per workgroup
+]
+
+
+@pytest.mark.parametrize("m,K,B", F4M_LOOP_CASES)
+def test_gemv_many_tokens_batch_loops(dev, m, K, B):
+    """The many-token product with several batches of row tiles per
+    workgroup (both parities of the batch count, the loop over pairs of
+    batches, the cap on tiles per workgroup), checked on sampled rows."""
+    _banner(f"gemv f4m batches m={m} K={K} B={B}")
+    rng = np.random.default_rng(m + K + B)
+    ldw = ((K + 31) // 32 + 3) // 4 * 4
+    packed = synth.random_sign_words(rng, m, K, ldw=ldw)
+    al = rng.standard_normal((B, K)).astype(np.float32)
+    al[:, rng.choice(K, size=max(1, K // 100), replace=False)] *= 20
+    s = rng.uniform(0.01, 0.03, m).astype(np.float32)
+    got = lq.gemv(torch.from_numpy(packed.view(np.int32)).to(dev), torch.from_numpy(s).to(dev),
+                  torch.from_numpy(al).to(dev), K).cpu().numpy()
+    rows = _sample_rows(m, np.random.default_rng(m))
+    ref = O.lifted_product(packed[rows], K, al, s[rows])
+    e = O.rel_err_colmax(got[:, rows], ref)
+    _banner(f"  rel err {e:.3e}")
+    assert np.isfinite(got).all()
+    assert e <= TOL_F32, e
+
+
 ROWS_CASES = [  # (m, K, B) on the one-launch kernel (every slice in one workgroup's LDS)
     (1, 4, 1),          # one row, one 4-position slice
     (4100, 20480, 1),   # 20 slices, the most one token takes; a last workgroup of one row tile
