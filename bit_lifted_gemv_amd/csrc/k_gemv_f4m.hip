@@ -40,9 +40,10 @@
 // whole kernel and streams its workgroup's row tiles through them; the
 // eight waves of a workgroup hold eight consecutive spans, and their partial
 // tiles are added in wave order through LDS.  The lifted dimension is split
-// into runs of eight spans, one per workgroup row; each split writes float32
-// partial sums to the workspace and a reduction kernel adds them in split
-// order and scales by s.  Deterministic.
+// into runs of eight spans (the grid's y) and the rows into groups of row
+// tiles (its x); each split writes float32 partial sums to the workspace and
+// a reduction kernel adds them in split order and scales by s.
+// Deterministic.
 #include "lq_internal.h"
 
 #include <type_traits>
@@ -52,14 +53,12 @@ namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kFar = 0x40000000u;     // past every weight range (<= 2^30 bytes)
 constexpr int kSpanWords = 16;
 constexpr int kPartBytes = 4 * 3 * 64 * 32;            // per span
 constexpr int kSpanBytes = kPartBytes + 4 * 16 * 4;    // parts, then exponents
-constexpr int kSpanVec = kSpanBytes / 16;
 
 // A per-lane value the compiler cannot fold (kept in a vector register).
 __device__ __forceinline__ uint32_t opaque_v(uint32_t v) {
