@@ -378,12 +378,13 @@ def test_gemv_few_tokens_scaling_is_exact(dev):
     assert np.array_equal(got[3], np.ldexp(base[3], -60))
 
 
-@pytest.mark.parametrize("B", [1, 3])
+@pytest.mark.parametrize("B", [1, 3, 16])
 def test_gemv_largest_weight_buffer(dev, B):
     """The largest weight matrix one call accepts, m * ldw * 4 = 2^30 bytes
     (4096 rows of 2^21 lifted positions: 32-bit buffer offsets up to their
-    limit, 2048 slices for one token), checked on sampled rows.  The signs
-    are drawn on the device by torch's seeded generator."""
+    limit, 2048 slices for one token; at 16 tokens 512 splits of K and the
+    cap on row tiles per workgroup), checked on sampled rows.  The signs are
+    drawn on the device by torch's seeded generator."""
     _banner(f"gemv largest weights 4096 x 2^21 B={B}")
     m, K = 4096, 1 << 21
     ldw = K // 32
@@ -420,14 +421,14 @@ def test_gemv_deterministic(dev):
 def test_gemv_token_counts_share_a_workspace(dev):
     """Calls with one m and different B (different kernels and splits) run on
     one workspace, each over what the previous call left in it."""
-    _banner("gemv B = 1, 4, 1, 2, 1 on one workspace")
+    _banner("gemv B = 1, 4, 16, 1, 2, 7, 1 on one workspace")
     rng = np.random.default_rng(5)
     m, K = 2050, 12288
     packed = synth.random_sign_words(rng, m, K)
     w = torch.from_numpy(packed.view(np.int32)).to(dev)
     s = rng.uniform(0.01, 0.03, m).astype(np.float32)
     sd = torch.from_numpy(s).to(dev)
-    for B in (1, 4, 1, 2, 1):
+    for B in (1, 4, 16, 1, 2, 7, 1):
         al = rng.standard_normal((B, K)).astype(np.float32)
         got = lq.gemv(w, sd, torch.from_numpy(al).to(dev), K).cpu().numpy()
         assert O.rel_err_colmax(got, O.lifted_product(packed, K, al, s)) <= TOL_F32, B
