@@ -577,9 +577,28 @@ def run_cases(torch, lq, synth, dev, tokens=0):
         lt = graph_time(torch, lambda k: lq.lift(rot.a, rot[k].t_inv, rot[k].M, L.d, L.D, out=al),
                         rot.R, 10, st)
         gb = gemv_bytes(m, L.K, B) / (g * 1e-3) / 1e9
-        res.append({"case": f"{cfg.name} {m}x{n} B={B}", "gemv_us": round(g * 1e3, 2),
-                    "gemv_GBs": round(gb, 1), "gemv_frac": round(gb / HBM_PEAK_GBS, 3),
-                    "lift_us": round(lt * 1e3, 2)})
+        rec = {"case": f"{cfg.name} {m}x{n} B={B}", "gemv_us": round(g * 1e3, 2),
+               "gemv_GBs": round(gb, 1), "gemv_frac": round(gb / HBM_PEAK_GBS, 3),
+               "lift_us": round(lt * 1e3, 2)}
+        if B >= 6:
+            # the layer's default for 6 - 16 tokens: the lift writes the
+            # GEMV's float8-part operand image, the GEMV reads it
+            img = torch.empty(lq.lift_parts_size(L.K), dtype=torch.uint8, device=dev)
+            lq.lift_parts(rot.a, rot[0].t_inv, rot[0].M, L.d, L.D, out=img)
+            for i in range(3):
+                lq.gemv_parts(rot[i].w, rot[i].s, img, L.K, B, out=out)
+            torch.cuda.synchronize()
+            gp = graph_time(torch, lambda k: lq.gemv_parts(rot[k].w, rot[k].s, img, L.K, B, out=out),
+                            rot.R, 10, st)
+            lp = graph_time(torch, lambda k: lq.lift_parts(rot.a, rot[k].t_inv, rot[k].M, L.d, L.D,
+                                                           out=img), rot.R, 10, st)
+            gpb = gemv_bytes(m, L.K, B) / (gp * 1e-3) / 1e9
+            rec["parts_path"] = {"gemv_us": round(gp * 1e3, 2), "gemv_GBs": round(gpb, 1),
+                                 "gemv_frac": round(gpb / HBM_PEAK_GBS, 3),
+                                 "lift_us": round(lp * 1e3, 2),
+                                 "lift_plus_gemv_us": round((gp + lp) * 1e3, 2),
+                                 "float32_path_lift_plus_gemv_us": round((g + lt) * 1e3, 2)}
+        res.append(rec)
         del rot
         torch.cuda.empty_cache()
     return res

@@ -44,6 +44,7 @@
 // tiles (its x); each split writes float32 partial sums to the workspace and
 // a reduction kernel adds them in split order and scales by s.
 // Deterministic.
+#include "f4m_image.h"
 #include "lq_internal.h"
 
 #include <type_traits>
@@ -56,9 +57,9 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kRsrcWord3 = 0x00020000u;
 constexpr uint32_t kFar = 0x40000000u;     // past every weight range (<= 2^30 bytes)
-constexpr int kSpanWords = 16;
-constexpr int kPartBytes = 4 * 3 * 64 * 32;            // per span
-constexpr int kSpanBytes = kPartBytes + 4 * 16 * 4;    // parts, then exponents
+using f4m::kSpanWords;
+using f4m::kPartBytes;
+using f4m::kSpanBytes;
 
 // A per-lane value the compiler cannot fold (kept in a vector register).
 __device__ __forceinline__ uint32_t opaque_v(uint32_t v) {
@@ -123,46 +124,7 @@ __global__ void __launch_bounds__(256) gemv_f4m_prep_kernel(const float* __restr
     x[4 * j + 2] = v.z;
     x[4 * j + 3] = v.w;
   }
-  uint32_t mb = 0;
-#pragma unroll
-  for (int j = 0; j < 32; ++j) mb = max(mb, __float_as_uint(x[j]) & 0x7FFFFFFFu);
-  mb = max(mb, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mb), 1)));
-  mb = max(mb, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mb), 2)));
-  mb = max(mb, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mb), 4)));
-  if (!live) return;
-  const int e = mb == 0 ? 0 : min(134 - static_cast<int>(mb >> 23), 119);
-  // dword (q', hh) of this half holds slots 8 q + 4 hh .. + 3 (q = 2 h + q'),
-  // i.e. positions 4 t + q for t = 4 hh .. 4 hh + 3
-  uint32_t d[3][4];
-#pragma unroll
-  for (int qq = 0; qq < 2; ++qq) {
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      float y[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) y[j] = ldexpf(x[4 * (4 * hh + j) + 2 * h + qq], e);
-#pragma unroll
-      for (int p = 0; p < 3; ++p) {
-        int v = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-        v = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], v, true);
-        d[p][2 * qq + hh] = static_cast<uint32_t>(v);
-        if (p < 2) {
-          y[0] = 16.f * (y[0] - __builtin_amdgcn_cvt_f32_fp8(v, 0));
-          y[1] = 16.f * (y[1] - __builtin_amdgcn_cvt_f32_fp8(v, 1));
-          y[2] = 16.f * (y[2] - __builtin_amdgcn_cvt_f32_fp8(v, 2));
-          y[3] = 16.f * (y[3] - __builtin_amdgcn_cvt_f32_fp8(v, 3));
-        }
-      }
-    }
-  }
-  uint8_t* span = ws + static_cast<int64_t>(c) * kSpanBytes;
-  const int blane = 16 * (2 * (g & 1) + h) + n;  // B lane group 2 (g % 2) + h
-  const int byte0 = 16 * (g >> 1);
-#pragma unroll
-  for (int p = 0; p < 3; ++p)
-    *reinterpret_cast<uint4*>(span + (((u * 3 + p) * 2 + (byte0 >> 4)) * 64 + blane) * 16) =
-        make_uint4(d[p][0], d[p][1], d[p][2], d[p][3]);
-  if (g == 0 && h == 0) reinterpret_cast<int*>(span + kPartBytes)[u * 16 + n] = e;
+  f4m::write_span_parts(x, live, u, n, g, h, ws + static_cast<int64_t>(c) * f4m::kSpanBytes);
 }
 
 // Main kernel.  A workgroup of 8 waves owns TW tiles of 16 rows and eight
@@ -418,14 +380,12 @@ size_t gemv_f4m_workspace_bytes(int64_t m, int64_t K, int64_t B) {
   return p.b_bytes + p.p_bytes;
 }
 
-hipError_t launch_gemv_f4m(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
-                           const float* a_lift, int64_t B, float* out, void* ws, hipStream_t st) {
-  const Plan p = plan(m, K, B);
-  uint8_t* bws = static_cast<uint8_t*>(ws);
-  float* partials = reinterpret_cast<float*>(bws + p.b_bytes);
-  const int prep_threads = p.nspans * 4 * 16 * 8;
-  hipLaunchKernelGGL(gemv_f4m_prep_kernel, dim3((prep_threads + 255) / 256), dim3(256), 0, st,
-                     a_lift, static_cast<int>(B), static_cast<int>(K), p.nspans, bws);
+namespace {
+
+// The product over the image bws (f4m_image.h) and the split reduction.
+hipError_t launch_product(const Plan& p, const uint32_t* w, int64_t m, int64_t K, int64_t ldw,
+                          const float* s, const uint8_t* bws, int64_t B, float* out,
+                          float* partials, hipStream_t st) {
   const void* fn = reinterpret_cast<const void*>(gemv_f4m_kernel<kT>);
   if (p.lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -441,6 +401,31 @@ hipError_t launch_gemv_f4m(const uint32_t* w, int64_t m, int64_t K, int64_t ldw,
                      dim3(256), 0, st, partials, s, out, static_cast<int>(m), static_cast<int>(B),
                      p.S);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv_f4m(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
+                           const float* a_lift, int64_t B, float* out, void* ws, hipStream_t st) {
+  const Plan p = plan(m, K, B);
+  uint8_t* bws = static_cast<uint8_t*>(ws);
+  float* partials = reinterpret_cast<float*>(bws + p.b_bytes);
+  const int prep_threads = p.nspans * 4 * 16 * 8;
+  hipLaunchKernelGGL(gemv_f4m_prep_kernel, dim3((prep_threads + 255) / 256), dim3(256), 0, st,
+                     a_lift, static_cast<int>(B), static_cast<int>(K), p.nspans, bws);
+  return launch_product(p, w, m, K, ldw, s, bws, B, out, partials, st);
+}
+
+size_t gemv_f4m_parts_workspace_bytes(int64_t m, int64_t K, int64_t B) {
+  return plan(m, K, B).p_bytes;
+}
+
+hipError_t launch_gemv_f4m_parts(const uint32_t* w, int64_t m, int64_t K, int64_t ldw,
+                                 const float* s, const void* parts, int64_t B, float* out,
+                                 void* ws, hipStream_t st) {
+  const Plan p = plan(m, K, B);
+  return launch_product(p, w, m, K, ldw, s, static_cast<const uint8_t*>(parts), B, out,
+                        static_cast<float*>(ws), st);
 }
 
 }  // namespace lq

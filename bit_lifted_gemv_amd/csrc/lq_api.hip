@@ -388,6 +388,70 @@ lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw, c
   return gemv_launch(w_packed, m, K, ldw, s, a_lift, B, out, workspace, as_stream(stream));
 }
 
+lq_status lq_lift_parts_size(int64_t K, size_t* bytes) {
+  if (!bytes) return fail(LQ_ERR_NULL, "bytes is null");
+  if (K < 1 || K > ((int64_t)1 << 24))
+    return fail(LQ_ERR_SHAPE, "K=%lld outside 1..2^24", (long long)K);
+  *bytes = lq::lift_parts_bytes(K);
+  return ok();
+}
+
+lq_status lq_lift_parts(const void* a, lq_dtype a_dtype, int64_t B, int64_t n,
+                        const void* t_inv, lq_dtype t_dtype, int32_t t_block,
+                        const float* M, int32_t d, int32_t D, void* parts,
+                        size_t parts_bytes, void* stream) {
+  if (!a || !t_inv || !M || !parts) return fail(LQ_ERR_NULL, "null pointer");
+  if (!valid_dtype(a_dtype) || !valid_dtype(t_dtype)) return fail(LQ_ERR_DTYPE, "unknown dtype");
+  if (a_dtype != t_dtype || a_dtype == LQ_F32)
+    return fail(LQ_ERR_DTYPE, "a and t_inv must share one 16-bit type");
+  if (t_block != 128)
+    return fail(LQ_ERR_UNSUPPORTED, "t_block=%d (only 128 is implemented)", (int)t_block);
+  if (B < 1 || B > 16 || n < 1)
+    return fail(LQ_ERR_SHAPE, "B=%lld (1..16) n=%lld", (long long)B, (long long)n);
+  if (n % 128) return fail(LQ_ERR_SHAPE, "n=%lld not a multiple of t_block", (long long)n);
+  if (d < 1 || n % d) return fail(LQ_ERR_SHAPE, "n=%lld not a multiple of d=%d", (long long)n, (int)d);
+  if (n > INT32_MAX || (int64_t)n / d * D > ((int64_t)1 << 24))
+    return fail(LQ_ERR_SHAPE, "n=%lld or K exceed the per-call limits", (long long)n);
+  if (!lq::lift_parts_applies(a_dtype, t_dtype, B, n, d, D))
+    return fail(LQ_ERR_UNSUPPORTED, "d=%d D=%d: needs d in {4, 8, 16, 32} and d <= D <= 256",
+                (int)d, (int)D);
+  const size_t need = lq::lift_parts_bytes((int64_t)n / d * D);
+  if (parts_bytes < need)
+    return fail(LQ_ERR_WORKSPACE, "parts buffer %zu bytes < %zu required", parts_bytes, need);
+  if (!aligned(t_inv, 16) || !aligned(a, 16) || !aligned(parts, 16))
+    return fail(LQ_ERR_ALIGN, "a, t_inv and parts must be 16-byte aligned");
+  if (!aligned(M, 4)) return fail(LQ_ERR_ALIGN, "misaligned M");
+  return hip_status(lq::launch_lift_parts(a, a_dtype, B, n, t_inv, M, d, D, parts,
+                                          as_stream(stream)),
+                    "lq_lift_parts launch");
+}
+
+lq_status lq_gemv_parts_workspace_size(int64_t m, int64_t K, int64_t B, size_t* bytes) {
+  if (!bytes) return fail(LQ_ERR_NULL, "bytes is null");
+  if (m < 1 || K < 1 || B < 1 || B > 16)
+    return fail(LQ_ERR_SHAPE, "m=%lld K=%lld B=%lld", (long long)m, (long long)K, (long long)B);
+  *bytes = lq::gemv_f4m_parts_workspace_bytes(m, K, B);
+  return ok();
+}
+
+lq_status lq_gemv_parts(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw,
+                        const float* s, const void* parts, size_t parts_bytes, int64_t B,
+                        float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  const lq_status st = gemv_check(w_packed, m, K, ldw, s, static_cast<const float*>(parts), B, out);
+  if (st != LQ_OK) return st;
+  if (parts_bytes < lq::lift_parts_bytes(K))
+    return fail(LQ_ERR_WORKSPACE, "parts buffer %zu bytes < %zu required", parts_bytes,
+                lq::lift_parts_bytes(K));
+  const size_t need = lq::gemv_f4m_parts_workspace_bytes(m, K, B);
+  if (!workspace) return fail(LQ_ERR_NULL, "workspace of %zu bytes required", need);
+  if (workspace_bytes < need)
+    return fail(LQ_ERR_WORKSPACE, "workspace %zu bytes < %zu required", workspace_bytes, need);
+  if (!aligned(workspace, 256)) return fail(LQ_ERR_ALIGN, "workspace must be 256-byte aligned");
+  return hip_status(lq::launch_gemv_f4m_parts(w_packed, m, K, ldw, s, parts, B, out, workspace,
+                                              as_stream(stream)),
+                    "lq_gemv_parts launch");
+}
+
 lq_status lq_stream_read(const void* buffer, size_t bytes, uint32_t* sink, void* stream) {
   if (bytes == 0) return ok();
   if (!buffer || !sink) return fail(LQ_ERR_NULL, "null pointer");

@@ -133,6 +133,20 @@ size_t gemv_f4m_workspace_bytes(int64_t m, int64_t K, int64_t B);
 hipError_t launch_gemv_f4m(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
                            const float* a_lift, int64_t B, float* out, void* ws, hipStream_t st);
 
+// The same product on an operand image written by the parts lift (no
+// preparation launch; the workspace holds only the split partial sums).
+size_t gemv_f4m_parts_workspace_bytes(int64_t m, int64_t K, int64_t B);
+hipError_t launch_gemv_f4m_parts(const uint32_t* w, int64_t m, int64_t K, int64_t ldw,
+                                 const float* s, const void* parts, int64_t B, float* out,
+                                 void* ws, hipStream_t st);
+
+// The lift into that image (k_lift_parts.hip): bytes for K lifted
+// positions, and whether the kernel takes the shape.
+size_t lift_parts_bytes(int64_t K);
+bool lift_parts_applies(lq_dtype a_dt, lq_dtype t_dt, int64_t B, int64_t n, int d, int D);
+hipError_t launch_lift_parts(const void* a, lq_dtype dt, int64_t B, int64_t n, const void* t_inv,
+                             const float* M, int d, int D, void* image, hipStream_t st);
+
 // Few-token GEMV on float4 sign / float8 activation-part matrix cores
 // (k_gemv_f4.hip), 1 <= B <= 5.
 size_t gemv_f4_workspace_bytes(int64_t m, int64_t K, int64_t B);

@@ -29,7 +29,8 @@ EXPORTS = ("lq_status_string", "lq_last_error", "lq_version", "lq_pack_signs", "
            "lq_encode_workspace_size", "lq_encode", "lq_softmin_workspace_size",
            "lq_softmin_grad", "lq_adam_update", "lq_gemm_decoded_workspace_size",
            "lq_gemm_decoded", "lq_layer_b1_workspace_size", "lq_layer_b1",
-           "lq_gemv_noalloc", "lq_stream_read")
+           "lq_gemv_noalloc", "lq_stream_read", "lq_lift_parts_size", "lq_lift_parts",
+           "lq_gemv_parts_workspace_size", "lq_gemv_parts")
 
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -64,6 +65,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "lq_gemm": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _i32, _i64, _vp, _vp]),
         "lq_gemv_noalloc": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _i64, _vp, _vp]),
         "lq_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
+        "lq_lift_parts_size": (_i32, [_i64, ctypes.POINTER(_sz)]),
+        "lq_lift_parts": (_i32, [_vp, _i32, _i64, _i64, _vp, _i32, _i32, _vp, _i32, _i32, _vp,
+                                 _sz, _vp]),
+        "lq_gemv_parts_workspace_size": (_i32, [_i64, _i64, _i64, ctypes.POINTER(_sz)]),
+        "lq_gemv_parts": (_i32, [_vp, _i64, _i64, _i64, _vp, _vp, _sz, _i64, _vp, _vp, _sz, _vp]),
         "lq_encode_workspace_size": (_i32, [_i32, _i32, ctypes.POINTER(_sz)]),
         "lq_encode": (_i32, [_vp, _i64, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
         "lq_softmin_workspace_size": (_i32, [_i64, _i32, _i32, ctypes.POINTER(_sz)]),
@@ -162,6 +168,28 @@ def lift(a: torch.Tensor, t_inv: torch.Tensor, M: torch.Tensor, d: int, D: int,
         out = torch.empty((B, K), dtype=out_dtype, device=a.device)
     check(lib().lq_lift_activations(_ptr(a), _dt(a), B, n, _ptr(t_inv), _dt(t_inv), t_block,
                                     _ptr(M), d, D, _ptr(out), _dt(out), _stream(stream)))
+    return out
+
+
+def lift_parts_size(K: int) -> int:
+    n = _sz(0)
+    check(lib().lq_lift_parts_size(K, ctypes.byref(n)))
+    return n.value
+
+
+def lift_parts(a: torch.Tensor, t_inv: torch.Tensor, M: torch.Tensor, d: int, D: int,
+               t_block: int = 128, out: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """a [B][n] and t_inv of one 16-bit type, M float [d][D] -> the operand
+    image of lq_gemv_parts (uint8, lq_lift_parts_size(n*D/d) bytes)."""
+    _dev(a, t_inv, M)
+    B, n = a.shape
+    nb = lift_parts_size(n // d * D)
+    if out is None:
+        out = torch.empty(nb, dtype=torch.uint8, device=a.device)
+    check(lib().lq_lift_parts(_ptr(a), _dt(a), B, n, _ptr(t_inv), _dt(t_inv), t_block, _ptr(M),
+                              d, D, _ptr(out), out.numel() * out.element_size(),
+                              _stream(stream)))
     return out
 
 
@@ -306,7 +334,8 @@ def workspace(nbytes: int, device: torch.device, tag: int = 0, stream=None) -> t
     grown on demand, zero-filled when allocated.  Calls on one stream run in
     order, so they may share it; calls on different streams get their own.
     The GEMV uses its row count as tag, the Kronecker lift -1, the encoder -2,
-    the soft-argmin objective -3, the decode-weights product -4."""
+    the soft-argmin objective -3, the decode-weights product -4, the GEMV on
+    the parts image -5."""
     key = (device.type, device.index, _stream(stream), tag)
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
@@ -336,6 +365,22 @@ def gemv(w_packed: torch.Tensor, s: torch.Tensor, a_lift: torch.Tensor, K: Optio
     ws = workspace(nws, a_lift.device, m, stream) if nws else None
     check(lib().lq_gemv(_ptr(w_packed), m, K, ldw, _ptr(s), _ptr(a_lift), B, _ptr(out), _ptr(ws),
                         nws, _stream(stream)))
+    return out
+
+
+def gemv_parts(w_packed: torch.Tensor, s: torch.Tensor, parts: torch.Tensor, K: int, B: int,
+               out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out [B][m] = s * (sigma @ a_hat^T) from the image of lift_parts."""
+    _dev(w_packed, s, parts)
+    m, ldw = w_packed.shape
+    if out is None:
+        out = torch.empty((B, m), dtype=torch.float32, device=parts.device)
+    n = _sz(0)
+    check(lib().lq_gemv_parts_workspace_size(m, K, B, ctypes.byref(n)))
+    ws = workspace(n.value, parts.device, -5, stream)
+    check(lib().lq_gemv_parts(_ptr(w_packed), m, K, ldw, _ptr(s), _ptr(parts),
+                              parts.numel() * parts.element_size(), B, _ptr(out), _ptr(ws),
+                              n.value, _stream(stream)))
     return out
 
 
@@ -395,13 +440,21 @@ class DeviceLayer:
     def from_synth(cls, L, device="cuda") -> "DeviceLayer":
         return cls(L.packed, L.M, L.t_inv, L.s, L.d, L.D, L.n, L.dtype, device)
 
+    def _parts_ok(self, a: torch.Tensor) -> bool:
+        """The lift into the GEMV's operand image takes a and T^-1 of one
+        16-bit type and d in {4, 8, 16, 32}."""
+        return (a.dtype in (torch.float16, torch.bfloat16) and a.dtype == self.t_inv.dtype
+                and self.d in (4, 8, 16, 32) and self.d <= self.D <= 256)
+
     def forward(self, a: torch.Tensor, gemm_dtype: torch.dtype = torch.float16,
                 path: str = "auto") -> torch.Tensor:
         """o [B][m]: lift then the GEMV (B <= 16) or the GEMM (larger B), the
-        faster paths at the workload shapes.  Paths: "gemv" / "gemm" force
+        faster paths at the workload shapes (6 - 16 tokens: the lift into the
+        GEMV's operand image, when it takes the shape).  Paths: "gemv" / "gemm" force
         those; "fused" the one-token layer with the lift inside the GEMV
         (lq_layer_b1); "decoded" u = T^-1 a (the lift with M = I_4) then the
-        decode-weights product."""
+        decode-weights product; "parts" the lift into the GEMV's float8-part
+        operand image, then the GEMV on it (lq_lift_parts, lq_gemv_parts)."""
         B = a.shape[0]
         if path == "fused":
             return layer_b1(a, self.t_inv, self.M, self.d, self.D, self.w, self.s)
@@ -409,6 +462,11 @@ class DeviceLayer:
             eye = torch.eye(4, dtype=torch.float32, device=a.device)
             u = lift(a, self.t_inv, eye, 4, 4, out_dtype=torch.float16)
             return gemm_decoded(self.w, self.s, self.M, self.d, self.D, u)
+        if path == "auto" and 6 <= B <= 16 and self._parts_ok(a):
+            path = "parts"
+        if path == "parts":
+            img = lift_parts(a, self.t_inv, self.M, self.d, self.D)
+            return gemv_parts(self.w, self.s, img, self.K, B)
         use_gemm = path == "gemm" or (path == "auto" and B > 16)
         if use_gemm:
             al = lift(a, self.t_inv, self.M, self.d, self.D, out_dtype=gemm_dtype)

@@ -278,6 +278,58 @@ lq_status lq_gemv(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * lq_lift_parts_size -- bytes of the operand image lq_lift_parts writes for
+ * K lifted positions (written to *bytes).
+ */
+lq_status lq_lift_parts_size(int64_t K, size_t* bytes);
+
+/*
+ * lq_lift_parts -- the lift of lq_lift_activations (关键设计 4: the small
+ * transform of the activations, done once per input; 关键设计 1 for M),
+ * written not as a_lift but as the operand image that lq_gemv_parts reads,
+ * so that the product needs no conversion launch of its own.
+ * a, t_inv: [B][n] and [n/t_block][t_block][t_block] of one 16-bit type
+ *           (LQ_F16 or LQ_BF16: their products are exact), 16-byte aligned.
+ * M:        float [d][D], 4-byte aligned.
+ * parts:    device buffer of >= lq_lift_parts_size(n*D/d) bytes, 16-byte
+ *           aligned, owned by the caller.  Layout (opaque to callers, fixed
+ *           by this library): per 512-position span of the lifted dimension
+ *           (whole groups of eight spans, padding spans zero), each token's
+ *           lifted values as three float8 (E4M3) parts in the order the
+ *           product's matrix operands hold them, then an int power-of-two
+ *           exponent per 128 positions and token; a value is p0 + p1/16 +
+ *           p2/256 times 2^-e, 12 significant bits.
+ * Requires 1 <= B <= 16, t_block == 128, n % 128 == 0, d in {4, 8, 16, 32},
+ * n % d == 0, d <= D <= 256.  Accumulation float32.  Errors as
+ * lq_lift_activations; LQ_ERR_WORKSPACE if parts_bytes is too small.
+ */
+lq_status lq_lift_parts(const void* a, lq_dtype a_dtype, int64_t B, int64_t n,
+                        const void* t_inv, lq_dtype t_dtype, int32_t t_block,
+                        const float* M, int32_t d, int32_t D, void* parts,
+                        size_t parts_bytes, void* stream);
+
+/*
+ * lq_gemv_parts_workspace_size -- bytes of workspace lq_gemv_parts needs
+ * (the partial sums over splits of K), written to *bytes.
+ */
+lq_status lq_gemv_parts_workspace_size(int64_t m, int64_t K, int64_t B, size_t* bytes);
+
+/*
+ * lq_gemv_parts -- lq_gemv on the image of lq_lift_parts instead of float
+ * lifted activations (关键设计 4, the 1-bit x float product), for 1 <= B <=
+ * 16 tokens on the matrix-core kernel of lq_gemv's 6 - 16 token range:
+ *   out[b][i] = s[i] * sum_{k<K} sigma_ik * a_hat[b][k].
+ * w_packed, ldw, s, out, K: as lq_gemv.  parts: the image of lq_lift_parts
+ * for the same K and B (parts_bytes >= lq_lift_parts_size(K)).  workspace:
+ * >= lq_gemv_parts_workspace_size bytes, 256-byte aligned, caller-owned, no
+ * initialisation needed; calls sharing it must not overlap.  Deterministic
+ * (fixed-order sums).  Errors as lq_gemv.
+ */
+lq_status lq_gemv_parts(const uint32_t* w_packed, int64_t m, int64_t K, int64_t ldw,
+                        const float* s, const void* parts, size_t parts_bytes, int64_t B,
+                        float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * lq_stream_read -- a plain read of `bytes` bytes of device memory at
  * `buffer` (16-byte aligned, bytes % 16 == 0), each byte once: the HBM read
  * rate the one-token lq_gemv (which reads each weight byte once) is

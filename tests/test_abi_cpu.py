@@ -124,6 +124,55 @@ def test_lift_validation(L):
     assert ok  # the happy path needs a GPU and is covered by the GPU tests
 
 
+def test_lift_parts_validation(L):
+    F16, BF16, F32 = lq.LQ_F16, lq.LQ_BF16, lq.LQ_F32
+    size = ctypes.c_size_t(0)
+    assert L.lq_lift_parts_size(3072, ctypes.byref(size)) == 0
+    # 3072 positions = 6 spans of 512, padded to whole groups of 8 spans
+    assert size.value == 8 * (4 * 3 * 64 * 32 + 4 * 16 * 4)
+    assert L.lq_lift_parts_size(0, ctypes.byref(size)) == 2
+    big = size.value
+
+    def call(a=P, adt=BF16, B=6, n=1280, t=P, tdt=BF16, tb=128, M=P, d=8, D=19, out=P, nb=big):
+        return L.lq_lift_parts(a, adt, B, n, t, tdt, tb, M, d, D, out, nb, None)
+
+    assert call(a=None) == 1
+    assert call(out=None) == 1
+    assert call(adt=F16) == 3          # a and t_inv of different types
+    assert call(adt=F32, tdt=F32) == 3
+    assert call(tb=64) == 5
+    assert call(B=0) == 2
+    assert call(B=17) == 2
+    assert call(n=1300) == 2
+    assert call(d=10, D=24) == 5       # d outside {4, 8, 16, 32}
+    assert call(d=8, D=4) == 5         # D < d
+    assert call(nb=big - 1) == 7       # image buffer too small
+    assert call(t=MIS) == 4
+    assert call(out=P + 8) == 4
+
+
+def test_gemv_parts_validation(L):
+    size = ctypes.c_size_t(0)
+    assert L.lq_gemv_parts_workspace_size(256, 3072, 16, ctypes.byref(size)) == 0
+    assert size.value >= 16 * 256 * 4
+    assert L.lq_gemv_parts_workspace_size(256, 3072, 17, ctypes.byref(size)) == 2
+    ws = size.value
+    img = ctypes.c_size_t(0)
+    assert L.lq_lift_parts_size(3072, ctypes.byref(img)) == 0
+
+    def call(w=P, m=256, K=3072, ldw=96, s=P, parts=P, nb=img.value, B=16, out=P, wsp=P, nws=ws):
+        return L.lq_gemv_parts(w, m, K, ldw, s, parts, nb, B, out, wsp, nws, None)
+
+    assert call(parts=None) == 1
+    assert call(wsp=None) == 1
+    assert call(B=0) == 2
+    assert call(B=17) == 2
+    assert call(ldw=95) == 2
+    assert call(nb=img.value - 16) == 7
+    assert call(nws=ws - 4) == 7
+    assert call(wsp=P + 16) == 4
+
+
 def test_lift_kron_validation(L):
     F16 = lq.LQ_F16
     nb = ctypes.c_size_t(0)
