@@ -59,3 +59,38 @@ def test_gemv_graph_replays_match_eager(dev, m, K, B):
             for ao in other:                    # eager calls over the same workspace
                 lq.gemv(w, s, ao, K)
             torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("m,n,d,D,B", [(8192, 8192, 8, 19, 16), (1000, 4096, 8, 16, 7)])
+def test_parts_path_graph_replays_match_eager(dev, m, n, d, D, B):
+    """lq_lift_parts + lq_gemv_parts captured together: three replays, eager
+    calls with other token counts on the same workspace in between, each
+    replay equal bit for bit to the eager pair."""
+    from bit_lifted_gemv_amd import lq
+    L = synth.make_layer(m, n, d, D, B, seed=m + B, dtype="bf16")
+    dl = lq.DeviceLayer.from_synth(L, device=dev)
+    a = lq.to_torch_16(L.a, "bf16").to(dev)
+    others = [lq.to_torch_16(synth.make_layer(64, n, d, D, b, seed=b, dtype="bf16").a,
+                             "bf16").to(dev) for b in (6, 16)]
+    img = torch.empty(lq.lift_parts_size(L.K), dtype=torch.uint8, device=dev)
+    out = torch.empty(B, m, device=dev)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        ref = dl.forward(a, path="parts").clone()
+        lq.lift_parts(a, dl.t_inv, dl.M, d, D, out=img)
+        lq.gemv_parts(dl.w, dl.s, img, L.K, B, out=out)   # the workspace exists before capture
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr, stream=st):
+            lq.lift_parts(a, dl.t_inv, dl.M, d, D, out=img)
+            lq.gemv_parts(dl.w, dl.s, img, L.K, B, out=out)
+        for r in range(3):
+            out.zero_()
+            img.zero_()
+            gr.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), f"replay {r}"
+            for ao in others:                   # eager calls over the same workspace
+                dl.forward(ao, path="parts")
+            torch.cuda.synchronize()
