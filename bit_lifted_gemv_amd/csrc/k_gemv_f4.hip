@@ -262,6 +262,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_f4_kernel(
 // a wave per (16-row tile, token); lane (row l % 16, part l / 16) adds slices
 // part, part + 4, ... in order (every load four whole 64-byte runs of the
 // tile, all in flight), then the four parts are added in a fixed order.
+// kChunk: slices of a lane in flight at once (the launch picks the smallest
+// power of two that covers the lane's slices, at most 32).
+template <int kChunk>
 __global__ void __launch_bounds__(256) gemv_f4_reduce_kernel(const float* __restrict__ partials,
                                                              const float* __restrict__ s,
                                                              float* __restrict__ out, int64_t m,
@@ -272,21 +275,21 @@ __global__ void __launch_bounds__(256) gemv_f4_reduce_kernel(const float* __rest
   const int64_t g = unit / NB;
   const int b = static_cast<int>(unit - g * NB);
   const int r = lane & 15, part = lane >> 4;
+  // every load of a chunk is issued before the first add: slices past S read
+  // the lane's last one again (an address known to be valid, no branch) and
+  // are not added
   const float* p = partials + ((g * S + part) * NB + b) * kGranuleRows + r;
   const int64_t qstep = 4 * (int64_t)NB * kGranuleRows;
+  const int qlast = part < S ? (S - 1 - part) / 4 : 0;   // this lane's last slice index
   float sum = 0.f;
-  int q = part;
-  for (; q + 12 < S; q += 16) {
-    const float v0 = p[0], v1 = p[qstep], v2 = p[2 * qstep], v3 = p[3 * qstep];
-    sum += v0;
-    sum += v1;
-    sum += v2;
-    sum += v3;
-    p += 4 * qstep;
-  }
-  for (; q < S; q += 4) {
-    sum += p[0];
-    p += qstep;
+  for (int i0 = 0; part + 4 * i0 < S; i0 += kChunk) {
+    float v[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) v[i] = p[min(i0 + i, qlast) * qstep];
+    // slices in increasing order, as many as this lane has
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i)
+      if (i0 + i <= qlast) sum += v[i];
   }
   sum += __shfl_xor(sum, 16);                   // parts 0 + 1, 2 + 3
   sum += __shfl_xor(sum, 32);                   // (0 + 1) + (2 + 3)
@@ -297,8 +300,20 @@ __global__ void __launch_bounds__(256) gemv_f4_reduce_kernel(const float* __rest
 void reduce_slices(const float* partials, const float* s, float* out, int64_t m, int S, int NB,
                    hipStream_t st) {
   const int64_t units = (m + kGranuleRows - 1) / kGranuleRows * NB;
-  hipLaunchKernelGGL(gemv_f4_reduce_kernel, dim3(static_cast<unsigned>((units + 3) / 4)), dim3(256),
-                     0, st, partials, s, out, m, S, NB, units);
+  const dim3 grid(static_cast<unsigned>((units + 3) / 4));
+  const int per_lane = (S + 3) / 4;
+  if (per_lane <= 4)
+    hipLaunchKernelGGL(gemv_f4_reduce_kernel<4>, grid, dim3(256), 0, st, partials, s, out, m, S,
+                       NB, units);
+  else if (per_lane <= 8)
+    hipLaunchKernelGGL(gemv_f4_reduce_kernel<8>, grid, dim3(256), 0, st, partials, s, out, m, S,
+                       NB, units);
+  else if (per_lane <= 16)
+    hipLaunchKernelGGL(gemv_f4_reduce_kernel<16>, grid, dim3(256), 0, st, partials, s, out, m, S,
+                       NB, units);
+  else
+    hipLaunchKernelGGL(gemv_f4_reduce_kernel<32>, grid, dim3(256), 0, st, partials, s, out, m, S,
+                       NB, units);
 }
 
 Sched make_sched(int64_t m, int64_t K) {

@@ -322,6 +322,9 @@ __global__ void __launch_bounds__(512, 1) gemv_f4m_kernel(
 
 // out[b][i] = -s[i] * sum over splits of partials[split][b][i], in split
 // order, for b < B.
+// kChunk: splits in flight at once (the launch picks the smallest power of
+// two that covers S, at most 16).
+template <int kChunk>
 __global__ void __launch_bounds__(256) gemv_f4m_reduce_kernel(const float* __restrict__ partials,
                                                               const float* __restrict__ s,
                                                               float* __restrict__ out, int m,
@@ -329,14 +332,16 @@ __global__ void __launch_bounds__(256) gemv_f4m_reduce_kernel(const float* __res
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const int64_t n = static_cast<int64_t>(B) * m;
   if (idx >= n) return;
-  // eight loads in flight at a time, added in split order
+  // every load of a chunk is issued before the first add: splits past S
+  // read the last one again (an address known to be valid, no branch) and
+  // are not added
   float v = 0.f;
-  for (int y0 = 0; y0 < S; y0 += 8) {
-    float p[8];
+  for (int y0 = 0; y0 < S; y0 += kChunk) {
+    float p[kChunk];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) p[j] = y0 + j < S ? partials[(y0 + j) * n + idx] : 0.f;
+    for (int j = 0; j < kChunk; ++j) p[j] = partials[static_cast<int64_t>(min(y0 + j, S - 1)) * n + idx];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < kChunk; ++j)
       if (y0 + j < S) v += p[j];
   }
   out[idx] = -s[idx % m] * v;
@@ -397,9 +402,20 @@ hipError_t launch_product(const Plan& p, const uint32_t* w, int64_t m, int64_t K
                      static_cast<int>(ldw), static_cast<int>((K + 31) / 32), bws, p.TW,
                      static_cast<int>(B), partials);
   const int64_t n = B * m;
-  hipLaunchKernelGGL(gemv_f4m_reduce_kernel, dim3(static_cast<unsigned>((n + 255) / 256)),
-                     dim3(256), 0, st, partials, s, out, static_cast<int>(m), static_cast<int>(B),
-                     p.S);
+  const dim3 rgrid(static_cast<unsigned>((n + 255) / 256));
+  const int mi = static_cast<int>(m), bi = static_cast<int>(B);
+  if (p.S <= 2)
+    hipLaunchKernelGGL(gemv_f4m_reduce_kernel<2>, rgrid, dim3(256), 0, st, partials, s, out, mi, bi,
+                       p.S);
+  else if (p.S <= 4)
+    hipLaunchKernelGGL(gemv_f4m_reduce_kernel<4>, rgrid, dim3(256), 0, st, partials, s, out, mi, bi,
+                       p.S);
+  else if (p.S <= 8)
+    hipLaunchKernelGGL(gemv_f4m_reduce_kernel<8>, rgrid, dim3(256), 0, st, partials, s, out, mi, bi,
+                       p.S);
+  else
+    hipLaunchKernelGGL(gemv_f4m_reduce_kernel<16>, rgrid, dim3(256), 0, st, partials, s, out, mi,
+                       bi, p.S);
   return hipGetLastError();
 }
 
