@@ -17,7 +17,7 @@
 // would arrive late), then issues the weight ring, and each wave converts
 // slices w, w + 8, ... (16 positions per lane, its own max over the slice);
 // one barrier.  The workgroup's granules (row tile, slice) are taken in
-// slice-major order and cut into 8 contiguous runs, one per wave, so a
+// slice-major order and cut into contiguous runs, one per wave, so a
 // wave's consecutive granules mostly share a slice and its B operands stay
 // in registers until the slice changes.  Each granule leaves its 16 rows'
 // sums for its slice in LDS; at the end the workgroup adds each row's slices
@@ -48,10 +48,13 @@ constexpr int kSliceBits = 1024;
 constexpr int kSliceBytes = kSliceBits / 8;     // 128 bytes of a row per slice
 constexpr int kSteps = kSliceBits / 128;        // 8 MFMA steps per slice
 constexpr uint32_t kNoLoad = 0x80000000u;       // past every buffer range: loads give 0
-constexpr int kWaves = 8;
-constexpr int kThreads = 64 * kWaves;
+// Waves per workgroup: 16 at one token (twice the waves to load and convert
+// the activations at the start: 70B up shape 19.3 -> 17.8 us), 8 for more
+// tokens (16 measured slower there).  The weight ring holds 32 granules per
+// workgroup either way (64 KB in flight per compute unit).
+constexpr int waves_for(int nb) { return nb == 1 ? 16 : 8; }
+constexpr int kRingPerWG = 32;
 constexpr int kRows = 16;
-constexpr int kDepth = 4;                       // granules of weights in flight per wave
 constexpr int kXFloats = 80;                    // activation registers per lane
 constexpr size_t kLdsBytes = 160 * 1024;
 
@@ -67,7 +70,8 @@ struct PlanR {
 
 // Dynamic LDS: parts [S][part_bytes] | column scale exponents [S][NB] int |
 // activation sums [S][NB] float | partial sums [RT][S][NB][16] float.
-template <int NB>
+template <int NB, int kWaves = waves_for(NB), int kThreads = 64 * kWaves,
+          int kDepth = kRingPerWG / kWaves>
 __global__ void __launch_bounds__(kThreads, 1) gemv_f4r_kernel(
     const uint32_t* __restrict__ w, int64_t m, int64_t K, int64_t ldw,
     const float* __restrict__ s, const float* __restrict__ ah, float* __restrict__ out,
@@ -269,7 +273,8 @@ hipError_t launch_r(const PlanR& p, const uint32_t* w, int64_t m, int64_t K, int
                                              static_cast<int>(p.lds));
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(gemv_f4r_kernel<NB>, dim3(p.G), dim3(kThreads), p.lds, st, w, m, K, ldw, s,
+  hipLaunchKernelGGL(gemv_f4r_kernel<NB>, dim3(p.G), dim3(64 * waves_for(NB)), p.lds, st, w, m, K,
+                     ldw, s,
                      a_lift, out, NG, p.RT, p.S, w_bytes, a_bytes);
   return hipGetLastError();
 }
@@ -286,7 +291,8 @@ bool gemv_f4r_applies(int64_t m, int64_t K, int64_t B) {
   // slices (80 KB of activations per workgroup) the slice-major kernel and
   // its reduction are faster (4096 x 28672: 11.0 against 11.8 us).
   if (B == 1 && p.S > 20) return false;
-  return p.S <= kWaves * xs_per_wave(static_cast<int>(B)) && p.lds <= kLdsBytes;
+  return p.S <= waves_for(static_cast<int>(B)) * xs_per_wave(static_cast<int>(B)) &&
+         p.lds <= kLdsBytes;
 }
 
 hipError_t launch_gemv_f4r(const uint32_t* w, int64_t m, int64_t K, int64_t ldw, const float* s,
