@@ -287,10 +287,11 @@ hipError_t launch_r(const PlanR& p, const uint32_t* w, int64_t m, int64_t K, int
 bool gemv_f4r_applies(int64_t m, int64_t K, int64_t B) {
   if (B < 1 || B > 5 || m < 1 || K < 1) return false;
   const PlanR p = plan_r(m, K, B);
-  // Every workgroup loads and converts every slice: at one token, past 20
-  // slices (80 KB of activations per workgroup) the slice-major kernel and
-  // its reduction are faster (4096 x 28672: 11.0 against 11.8 us).
-  if (B == 1 && p.S > 20) return false;
+  // Every workgroup loads and converts every slice: at one token the one
+  // launch (16 waves) is taken up to 40 slices (160 KB of activations per
+  // workgroup; 4096 x 28672, 28 slices: 10.2 us against 10.8 us for the
+  // slice-major kernel and its reduction; with 8 waves it lost past 20).
+  if (B == 1 && p.S > 40) return false;
   return p.S <= waves_for(static_cast<int>(B)) * xs_per_wave(static_cast<int>(B)) &&
          p.lds <= kLdsBytes;
 }

@@ -24,7 +24,8 @@ def dev():
 
 GRAPH_CASES = [  # (m, K, B): the path each one takes
     (8192, 19456, 1),    # one launch (19 slices)
-    (4096, 28672, 1),    # slice-major kernel and its reduction (28 slices)
+    (2048, 68096, 1),    # slice-major kernel and its reduction (67 slices)
+    (4096, 28672, 1),    # one launch with 16 waves (28 slices)
     (8192, 19456, 4),    # slice-major kernel and its reduction, four tokens
     (8192, 19456, 16),   # preparation, product with register-held operands, reduction
     (4104, 9216, 7),     # the same at 7 tokens, a ragged last row tile

@@ -201,6 +201,7 @@ GEMV_CASES = [  # (m, K, B): ragged rows, slices and token groups
     # one token: a single slice (no split), a 4-position last slice, a ragged
     # 8-row granule, and more slices than workgroups (ranges over > 2 slices)
     (1000, 1024, 1), (37, 1028, 1), (8193, 2048, 1), (64, 300000, 1),
+    (300, 41984, 1),    # 41 slices: one past the one-launch kernel's limit at one token
 ]
 
 
@@ -322,7 +323,8 @@ def test_gemv_many_tokens_batch_loops(dev, m, K, B):
 
 ROWS_CASES = [  # (m, K, B) on the one-launch kernel (every slice in one workgroup's LDS)
     (1, 4, 1),          # one row, one 4-position slice
-    (4100, 20480, 1),   # 20 slices, the most one token takes; a last workgroup of one row tile
+    (4100, 20480, 1),   # 20 slices; a last workgroup of one row tile
+    (2100, 40960, 1),   # 40 slices, the most one token takes
     (4097, 3072, 1),    # a ragged last row tile of one row
     (300, 16384, 2),    # 16 slices, the most two tokens take
     (33, 7200, 3),      # a ragged last slice
