@@ -15,7 +15,8 @@
 // position and token).  The start loads the activations first and waits for
 // them before any weight load is issued (behind a flood of weight misses they
 // would arrive late), then issues the weight ring, and each wave converts
-// slices w, w + 8, ... (16 positions per lane, its own max over the slice);
+// slices w, w + W, ... of the W waves (16 positions per lane, its own max
+// over the slice);
 // one barrier.  The workgroup's granules (row tile, slice) are taken in
 // slice-major order and cut into contiguous runs, one per wave, so a
 // wave's consecutive granules mostly share a slice and its B operands stay
@@ -107,7 +108,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemv_f4r_kernel(
   const uint32_t lane_off1 = lane_off0 + 64;
   const uint32_t wg_off = static_cast<uint32_t>(rt0) * kRows * row_bytes;
 
-  // 1. Activations of the slices this wave converts (w, w + 8, ...), lane l
+  // 1. Activations of the slices this wave converts (w, w + kWaves, ...), lane l
   // holding positions 16 l .. 16 l + 15 of each.
   f32x4 xv[XS][NB][4];
 #pragma unroll
