@@ -154,3 +154,16 @@ def test_full_size_case_through_parts(dev, cfg, si, shape, B):
     e = O.rel_err_colmax(got[:, rows], ref)
     _banner(f"  rel err {e:.3e}")
     assert e <= TOL_F32, e
+
+
+def test_image_columns_past_B_are_zero(dev):
+    """lq_lift_parts writes all 16 token columns, zero past B: the product on
+    that image for more tokens than were lifted gives the lifted tokens'
+    outputs unchanged and zero for the rest."""
+    L = synth.make_layer(200, 2048, 8, 19, 5, seed=11, dtype="bf16")
+    dl = lq.DeviceLayer.from_synth(L, device=dev)
+    img = lq.lift_parts(lq.to_torch_16(L.a, "bf16").to(dev), dl.t_inv, dl.M, 8, 19)
+    five = lq.gemv_parts(dl.w, dl.s, img, L.K, 5).cpu()
+    sixteen = lq.gemv_parts(dl.w, dl.s, img, L.K, 16).cpu()
+    assert torch.equal(sixteen[:5], five)
+    assert not sixteen[5:].abs().any()
