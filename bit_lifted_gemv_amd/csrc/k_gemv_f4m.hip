@@ -323,7 +323,7 @@ __global__ void __launch_bounds__(512, 1) gemv_f4m_kernel(
 // out[b][i] = -s[i] * sum over splits of partials[split][b][i], in split
 // order, for b < B.
 // kChunk: splits in flight at once (the launch picks the smallest power of
-// two that covers S, at most 16).
+// two that covers S, at most 32).
 template <int kChunk>
 __global__ void __launch_bounds__(256) gemv_f4m_reduce_kernel(const float* __restrict__ partials,
                                                               const float* __restrict__ s,
@@ -413,8 +413,11 @@ hipError_t launch_product(const Plan& p, const uint32_t* w, int64_t m, int64_t K
   else if (p.S <= 8)
     hipLaunchKernelGGL(gemv_f4m_reduce_kernel<8>, rgrid, dim3(256), 0, st, partials, s, out, mi, bi,
                        p.S);
-  else
+  else if (p.S <= 16)
     hipLaunchKernelGGL(gemv_f4m_reduce_kernel<16>, rgrid, dim3(256), 0, st, partials, s, out, mi,
+                       bi, p.S);
+  else
+    hipLaunchKernelGGL(gemv_f4m_reduce_kernel<32>, rgrid, dim3(256), 0, st, partials, s, out, mi,
                        bi, p.S);
   return hipGetLastError();
 }
