@@ -6,14 +6,14 @@
 // and then, instead of writing a_hat, the float8 parts and exponents of
 // f4m_image.h, so that the GEMV needs no preparation launch.
 //
-// One workgroup of 4 waves per span (512 lifted positions) and group of 4
-// (8 when there are more spans than a quarter of the compute units) of the
+// One workgroup of 4 waves per span (512 lifted positions) and group of 2,
+// 4 or 8 (as the span count allows about one workgroup per compute unit) of the
 // image's 16 token columns (every column is written, zero past B): the
 // conversion is a chain of dependent steps per value, so the work is spread
 // over more compute units than there are spans.  The workgroup
 // computes u for its tokens and the channels of every lift group that
 // overlaps the span (rounded out to 16-channel tiles, which never straddle a
-// 128-block) on v_mfma_f32_16x16x32_{f16,bf16}: A = 16 token rows (4 or 8 live)
+// 128-block) on v_mfma_f32_16x16x32_{f16,bf16}: A = 16 token rows (2, 4 or 8 live)
 // x 32 positions of a, B = 32 positions x 16 channels of T^-1 rows, both
 // exact 16-bit values, float32 sums; the tiles are dealt to the waves round
 // robin, all loads of a wave issued before its products.  u goes to LDS;
@@ -62,8 +62,8 @@ __host__ __device__ constexpr int max_span_channels(int d, int D) {
   return ((f4m::kSpanPositions - 1) / D + 2) * d + 32;
 }
 
-// DT: type of a and T^-1; DD = d; kTok: token columns per workgroup (4 or
-// 8).  cpad: floats per token row of u in LDS.
+// DT: type of a and T^-1; DD = d; kTok: token columns per workgroup (2, 4
+// or 8).  cpad: floats per token row of u in LDS.
 template <int DT, int DD, int kTok>
 __global__ void __launch_bounds__(kThreads) lift_parts_kernel(
     const uint16_t* __restrict__ a, const uint16_t* __restrict__ t_inv,
@@ -116,10 +116,9 @@ __global__ void __launch_bounds__(kThreads) lift_parts_kernel(
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) acc = mfma16x32<DT>(af[ks], bt[ks], acc);
     // D[token][channel]: lane (i, kg) holds channel i, tokens 4 kg .. 4 kg + 3
-    if (4 * kg < kTok) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) su[(4 * kg + e) * cpad + 16 * t + li] = acc[e];
-    }
+    for (int e = 0; e < 4; ++e)
+      if (4 * kg + e < kTok) su[(4 * kg + e) * cpad + 16 * t + li] = acc[e];
   };
   // kTW tiles per wave per round (one round at the workload shapes), every
   // load of a round issued before its MFMAs.
@@ -207,12 +206,13 @@ hipError_t launch_tok(const void* a, int64_t B, int64_t n, const void* t_inv, co
   return hipGetLastError();
 }
 
-// Four token columns per workgroup while that keeps the grid within about
-// one workgroup per compute unit, else eight.
+// Two token columns per workgroup while that keeps the grid within about
+// one workgroup per compute unit, else four, else eight.
 template <int DT, int DD>
 hipError_t launch_dd(const void* a, int64_t B, int64_t n, const void* t_inv, const float* M,
                      int D, void* image, hipStream_t st) {
   const int64_t spans = f4m::image_spans(n / DD * D);
+  if (spans * 8 <= num_cus()) return launch_tok<DT, DD, 2>(a, B, n, t_inv, M, D, image, st);
   if (spans * 4 <= num_cus()) return launch_tok<DT, DD, 4>(a, B, n, t_inv, M, D, image, st);
   return launch_tok<DT, DD, 8>(a, B, n, t_inv, M, D, image, st);
 }
